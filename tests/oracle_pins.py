@@ -1,0 +1,225 @@
+"""Checks that pin the CPU oracle to facts fixed by the definition and by mathematics.
+
+Each ``pin_*`` takes an attention implementation with the oracle's signature
+``impl(q, k, v, scale, causal=False, kv_seqlens=None, return_p=False)`` and raises
+AssertionError when the implementation disagrees with:
+
+* brute force at 50 significant digits (mpmath), P = e^S / sum e^S with no max shift;
+* hand-worked cases (tests/golden/worked_examples.json);
+* closed forms: Q = 0 gives the mean of the allowed V rows and lse = ln |A_i|; a single allowed
+  key returns its V row and lse = its score; constant V returns that constant; causal row 0
+  returns V_0;
+* invariants: rows of P sum to 1, masked keys get exactly zero weight, permuting keys with
+  their values changes nothing, shifting every key by t leaves O unchanged and moves lse by
+  scale * q.t;
+* stability: scores of magnitude ~1000 stay finite and exact.
+
+The same pins run against deliberately broken copies of the oracle (tests/test_oracle_mutants.py)
+to show that a plausible mistake fails at least one of them.
+"""
+
+from __future__ import annotations
+
+import json
+import os
+
+import mpmath
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_examples.json")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def brute_force_mp(q, k, v, scale, causal, lens, digits=50):
+    """Definition evaluated in mpmath at ``digits`` significant digits, with no max shift."""
+    mpmath.mp.dps = digits
+    bsz, heads, nq, d = q.shape
+    nk = k.shape[2]
+    o = np.zeros((bsz, heads, nq, v.shape[3]))
+    lse = np.zeros((bsz, heads, nq))
+    for b in range(bsz):
+        length = nk if lens is None else min(max(int(lens[b]), 0), nk)
+        for h in range(heads):
+            for i in range(nq):
+                allowed = [j for j in range(nk) if j < length and (not causal or j <= i)]
+                if not allowed:
+                    o[b, h, i] = 0.0
+                    lse[b, h, i] = -np.inf
+                    continue
+                sc = {}
+                for j in allowed:
+                    acc = mpmath.mpf(0)
+                    for t in range(d):
+                        acc += mpmath.mpf(float(q[b, h, i, t])) * mpmath.mpf(float(k[b, h, j, t]))
+                    sc[j] = mpmath.mpf(float(scale)) * acc
+                ex = {j: mpmath.exp(sc[j]) for j in allowed}
+                z = mpmath.fsum(ex.values())
+                for t in range(v.shape[3]):
+                    o[b, h, i, t] = float(mpmath.fsum(ex[j] * mpmath.mpf(float(v[b, h, j, t]))
+                                                      for j in allowed) / z)
+                lse[b, h, i] = float(mpmath.log(z))
+    return o, lse
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin), f"{what}: finiteness differs"
+    assert np.array_equal(a[~fin], b[~fin]), f"{what}: infinities differ"
+    if fin.any():
+        err = np.max(np.abs(a[fin] - b[fin]) / np.maximum(1.0, np.abs(b[fin])))
+        assert err <= tol, f"{what}: error {err:.3e} > {tol:.1e}"
+
+
+def pin_brute_force(impl):
+    cases = [
+        # (B, H, Nq, Nk, d, causal, lens, seed)
+        (1, 1, 3, 5, 2, False, None, 1),
+        (2, 1, 4, 7, 3, False, [7, 3], 2),
+        (1, 2, 6, 6, 4, True, None, 3),
+        (2, 2, 5, 5, 3, True, [5, 2], 4),
+        (2, 1, 3, 8, 4, False, [0, 1], 5),
+        (1, 1, 8, 8, 1, True, [6], 6),
+    ]
+    for bsz, heads, nq, nk, d, causal, lens, seed in cases:
+        r = _rng(seed)
+        q = r.standard_normal((bsz, heads, nq, d))
+        k = r.standard_normal((bsz, heads, nk, d))
+        v = r.standard_normal((bsz, heads, nk, d + 1))
+        scale = 0.7
+        o, lse = impl(q, k, v, scale, causal, lens)
+        o_ref, lse_ref = brute_force_mp(q, k, v, scale, causal, lens)
+        _close(o, o_ref, 1e-12, f"O brute force case seed={seed}")
+        _close(lse, lse_ref, 1e-12, f"lse brute force case seed={seed}")
+
+
+def pin_golden(impl):
+    with open(GOLDEN) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        q = np.array(c["q"], dtype=np.float64)
+        k = np.array(c["k"], dtype=np.float64)
+        v = np.array(c["v"], dtype=np.float64)
+        o_ref = np.array(c["o"], dtype=np.float64)
+        lse_ref = np.array([[[float(x) for x in row] for row in hh] for hh in c["lse"]])
+        o, lse = impl(q, k, v, c["scale"], c["causal"], c["kv_seqlens"])
+        _close(o, o_ref, 1e-12, f"O golden {c['name']}")
+        _close(lse, lse_ref, 1e-12, f"lse golden {c['name']}")
+
+
+def pin_zero_query_is_mean(impl):
+    r = _rng(11)
+    for causal, lens in ((False, [9, 4, 1]), (True, None), (True, [9, 5, 2])):
+        bsz, nq = 3, 9
+        nk = nq
+        q = np.zeros((bsz, 2, nq, 5))
+        k = r.standard_normal((bsz, 2, nk, 5))
+        v = r.standard_normal((bsz, 2, nk, 3))
+        o, lse = impl(q, k, v, 0.9, causal, lens)
+        for b in range(bsz):
+            length = nk if lens is None else lens[b]
+            for i in range(nq):
+                allowed = [j for j in range(nk) if j < length and (not causal or j <= i)]
+                if not allowed:
+                    continue
+                _close(o[b, :, i], v[b][:, allowed].mean(axis=1), 1e-14, "Q=0 mean")
+                assert np.all(lse[b, :, i] == np.log(len(allowed))), "Q=0 lse = ln|A|"
+
+
+def pin_single_key(impl):
+    r = _rng(12)
+    q = r.standard_normal((2, 2, 4, 6))
+    k = r.standard_normal((2, 2, 5, 6))
+    v = r.standard_normal((2, 2, 5, 6))
+    o, lse = impl(q, k, v, 0.3, False, [1, 1])
+    _close(o, np.broadcast_to(v[:, :, :1, :], o.shape), 1e-15, "single key O = V_0")
+    s0 = 0.3 * np.einsum("bhid,bhd->bhi", q, k[:, :, 0, :])
+    _close(lse, s0, 1e-14, "single key lse = S_i0")
+    # A single key without any length argument.
+    o1, lse1 = impl(q, k[:, :, :1], v[:, :, :1], 0.3, False, None)
+    _close(o1, np.broadcast_to(v[:, :, :1, :], o1.shape), 1e-15, "Nk=1 O = V_0")
+    _close(lse1, s0, 1e-14, "Nk=1 lse")
+
+
+def pin_constant_v(impl):
+    r = _rng(13)
+    q = r.standard_normal((1, 3, 7, 4))
+    k = r.standard_normal((1, 3, 7, 4))
+    v = np.full((1, 3, 7, 4), -2.75)
+    for causal in (False, True):
+        o, _ = impl(q, k, v, 1.3, causal, None)
+        _close(o, np.full_like(o, -2.75), 1e-14, "constant V")
+
+
+def pin_causal_first_row(impl):
+    r = _rng(14)
+    q = r.standard_normal((2, 2, 6, 3))
+    k = r.standard_normal((2, 2, 6, 3))
+    v = r.standard_normal((2, 2, 6, 3))
+    o, lse = impl(q, k, v, 0.5, True, None)
+    _close(o[:, :, 0], v[:, :, 0], 1e-15, "causal row 0 O = V_0")
+    _close(lse[:, :, 0], 0.5 * np.sum(q[:, :, 0] * k[:, :, 0], axis=-1), 1e-14, "causal lse_0")
+
+
+def pin_probabilities(impl):
+    r = _rng(15)
+    q = r.standard_normal((2, 2, 6, 4))
+    k = r.standard_normal((2, 2, 6, 4))
+    v = r.standard_normal((2, 2, 6, 4))
+    lens = [6, 3]
+    for causal in (False, True):
+        o, lse, p = impl(q, k, v, 0.8, causal, lens, return_p=True)
+        for b in range(2):
+            for i in range(6):
+                allowed = np.array([j < lens[b] and (not causal or j <= i) for j in range(6)])
+                assert np.all(p[b, :, i, ~allowed] == 0.0), "masked keys must have zero weight"
+                assert np.all(p[b, :, i, allowed] > 0.0), "allowed keys have positive weight"
+                _close(p[b, :, i].sum(axis=-1), np.ones(2), 1e-14, "rows of P sum to 1")
+        _close(np.einsum("bhij,bhjd->bhid", p, v), o, 1e-14, "O = P V")
+
+
+def pin_key_permutation(impl):
+    r = _rng(16)
+    q = r.standard_normal((2, 2, 5, 4))
+    k = r.standard_normal((2, 2, 9, 4))
+    v = r.standard_normal((2, 2, 9, 4))
+    perm = r.permutation(9)
+    o1, lse1 = impl(q, k, v, 0.6, False, None)
+    o2, lse2 = impl(q, k[:, :, perm], v[:, :, perm], 0.6, False, None)
+    _close(o2, o1, 1e-13, "key permutation O")
+    _close(lse2, lse1, 1e-13, "key permutation lse")
+
+
+def pin_key_shift(impl):
+    r = _rng(17)
+    q = r.standard_normal((1, 2, 6, 4))
+    k = r.standard_normal((1, 2, 6, 4))
+    v = r.standard_normal((1, 2, 6, 4))
+    t = r.standard_normal(4)
+    for causal, lens in ((False, [4]), (True, None)):
+        o1, lse1 = impl(q, k, v, 0.7, causal, lens)
+        o2, lse2 = impl(q, k + t, v, 0.7, causal, lens)
+        _close(o2, o1, 1e-13, "key shift O")
+        _close(lse2, lse1 + 0.7 * (q @ t), 1e-13, "key shift lse")
+
+
+def pin_large_scores(impl):
+    r = _rng(18)
+    q = 20.0 * r.standard_normal((1, 1, 4, 3))
+    k = 20.0 * r.standard_normal((1, 1, 6, 3))
+    v = r.standard_normal((1, 1, 6, 3))
+    o, lse = impl(q, k, v, 1.0, False, None)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), "large scores stay finite"
+    o_ref, lse_ref = brute_force_mp(q, k, v, 1.0, False, None)
+    _close(o, o_ref, 1e-12, "large scores O")
+    _close(lse, lse_ref, 1e-12, "large scores lse")
+
+
+ALL_PINS = [pin_brute_force, pin_golden, pin_zero_query_is_mean, pin_single_key, pin_constant_v,
+            pin_causal_first_row, pin_probabilities, pin_key_permutation, pin_key_shift,
+            pin_large_scores]
