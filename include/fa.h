@@ -1,0 +1,79 @@
+/*
+ * fa.h -- C ABI of libfa, an exact-attention forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed. For every batch b, head h and query row i:
+ *   allowed keys  A_i = { j : j < L_b and (causal == 0 or j <= i) }
+ *   S_ij = scale * q_i . k_j  (j in A_i),  P_i = softmax over A_i of S_i,  O_i = sum_j P_ij v_j,
+ *   lse_i = ln sum_{j in A_i} exp(S_ij)   (natural log);  A_i empty -> O_i = 0, lse_i = -inf.
+ * This is standard softmax attention (page "FlashAttention：把注意力从公式写成数据流", opening
+ * paragraph; page "FlashAttention 与边缘设备上的注意力内存瓶颈", section "2 标准 attention 的问题"),
+ * computed tile by tile with an online softmax so that S and P never reach device memory
+ * (same pages: sections "分块与在线 softmax" and "3.1 Tiling" / "3.2 Online Softmax"). Masked
+ * and padded keys never enter the normalisation (page "FlashAttention：把注意力从公式写成数据流",
+ * section "精度、掩码和边界情况"). The logsumexp output is part of this library's contract.
+ *
+ * Layout (all row-major, d fastest, no strides):
+ *   q, o : [B][H][Nq][d]      k, v : [B][H][Nk][d]      lse : [B][H][Nq] fp32
+ *   kv_seqlens : int32 [B] valid key count per sequence, clamped to [0, Nk] on the device;
+ *                NULL means every sequence has Nk valid keys.
+ * q, k, v and o must be 16-byte aligned; lse and kv_seqlens 4-byte aligned.
+ *
+ * Ownership. Every pointer is device memory owned by the caller. The library reads q, k, v and
+ * kv_seqlens, writes only o and lse (and, for Nq == 1, a workspace it allocates and frees
+ * stream-ordered on `stream`), and keeps no pointer after the call. Key slots at or past L_b are
+ * never read, so they may hold anything.
+ *
+ * Streams and errors. `stream` is a hipStream_t (NULL = the default stream). All work is enqueued
+ * on it; the call never synchronises. Arguments are checked before anything is enqueued: on any
+ * error nothing is launched and a negative fa_status_t comes back. Faults that happen inside a
+ * kernel surface at the caller's next synchronisation, as for any stream-ordered API.
+ * Calls on different streams are independent (no shared mutable state).
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = -1, /* null pointer, negative size, misalignment, non-finite scale */
+  FA_ERR_UNSUPPORTED = -2,      /* d not in {64, 128}; causal with Nq != Nk; sizes past int32  */
+  FA_ERR_HIP = -3               /* the HIP runtime refused a launch or an allocation           */
+} fa_status_t;
+
+/*
+ * fa_fwd -- bf16 attention forward: q, k, v, o hold bf16 values (raw 16-bit patterns);
+ * lse is fp32. Arithmetic: bf16 products on the matrix cores with fp32 accumulation, softmax in
+ * fp32, O rounded to bf16 (nearest even) once at the end.
+ *   B, H >= 0; Nq, Nk >= 0; d in {64, 128}; scale finite (any sign); causal in {0, 1} and,
+ *   if set, Nq == Nk. B*H*Nq == 0 is a valid no-op; Nk == 0 gives O = 0 and lse = -inf.
+ *   Nq == 1 runs the split-KV decode kernels (one query per (b, h)); any other Nq runs the
+ *   tiled prefill kernel.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+           const int32_t* kv_seqlens, void* stream);
+
+/*
+ * fa_fwd_f32 -- the same operation with fp32 q, k, v and o (fp32 products and accumulation on
+ * the matrix cores, fp32 softmax). Same argument rules as fa_fwd; every Nq runs the tiled kernel.
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int Nq, int Nk, int d, float scale, int causal,
+               const int32_t* kv_seqlens, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* Detail of the last failed call on this host thread ("" if none). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

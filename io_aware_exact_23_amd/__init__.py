@@ -1,0 +1,144 @@
+"""Exact attention forward for AMD Instinct MI355X (gfx950): Python binding of libfa.
+
+The work is done by the HIP kernels in ``libfa.so`` (built in-tree by
+``io_aware_exact_23_amd.build``); this module only marshals arguments through ctypes. PyTorch
+provides device memory and the stream. There is no fallback: if the library is missing, every
+call raises ``FaError``.
+
+Entry points mirror the C ABI in ``include/fa.h``:
+
+* ``fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, stream)`` -- bf16
+* ``fa_fwd_f32(...)``                                                          -- fp32
+* ``fa_status_string(status)``, ``fa_last_error()``
+
+Pointer arguments accept a torch tensor (its ``data_ptr()``), an int address or None; ``stream``
+accepts a ``torch.cuda.Stream``, an int handle or None (the current torch stream).
+``attention(q, k, v, ...)`` allocates O and lse with torch and calls the right entry point.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_status_string", "fa_last_error", "attention",
+           "library_path", "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfa.so")
+_lib = None
+
+FA_OK = 0
+FA_ERR_INVALID_ARGUMENT = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_HIP = -3
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libfa status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libfa.so once; raise FaError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise FaError(FA_ERR_HIP, f"{_LIB_PATH} not found: build it with "
+                                  "`python -m io_aware_exact_23_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    sig = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp, vp]
+    for name in ("fa_fwd", "fa_fwd_f32"):
+        fn = getattr(lib, name)
+        fn.argtypes = sig
+        fn.restype = ci
+    lib.fa_status_string.argtypes = [ci]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr() if x.numel() > 0 else None
+    return int(x)
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream
+    return int(s)
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_last_error() -> str:
+    return load_library().fa_last_error().decode()
+
+
+def _call(name, q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, stream):
+    lib = load_library()
+    st = getattr(lib, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                            int(Nq), int(Nk), int(d), float(scale), int(causal),
+                            _ptr(kv_seqlens), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, f"{fa_status_string(st)} ({fa_last_error()})")
+
+
+def fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens=None, stream=None) -> None:
+    """bf16 forward; see include/fa.h for the contract."""
+    _call("fa_fwd", q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, stream)
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens=None, stream=None) -> None:
+    """fp32 forward; see include/fa.h for the contract."""
+    _call("fa_fwd_f32", q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, stream)
+
+
+def attention(q, k, v, scale: Optional[float] = None, causal: bool = False, kv_seqlens=None,
+              out=None, lse=None, stream=None) -> Tuple["object", "object"]:
+    """O, lse for device tensors q [B,H,Nq,d] and k, v [B,H,Nk,d] (bf16 or fp32, contiguous)."""
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+        raise ValueError("k and v must be [B, H, Nk, d] matching q")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    if kv_seqlens is not None:
+        if kv_seqlens.dtype != torch.int32 or not kv_seqlens.is_cuda or kv_seqlens.numel() != B:
+            raise ValueError("kv_seqlens must be an int32 device tensor of length B")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
+    fn(q, k, v, out, lse, B, H, Nq, Nk, d, scale, int(bool(causal)), kv_seqlens, stream)
+    return out, lse

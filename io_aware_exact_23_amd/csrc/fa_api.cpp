@@ -1,0 +1,153 @@
+// fa_api.cpp -- the C ABI of libfa: argument checks, dispatch and launches (host side).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <limits>
+
+#include "fa.h"
+#include "fa_params.h"
+
+namespace fa {
+hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);
+int prefill_bf16_rows_per_wg(int d);
+int decode_chunk();
+}  // namespace fa
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* msg) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+  return status;
+}
+
+int fail_hip(hipError_t e, const char* where) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, hipGetErrorString(e));
+  return FA_ERR_HIP;
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+// Checks shared by both entry points. Returns FA_OK, an error, or 1 for "valid no-op".
+int check_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                 const int32_t* kv_seqlens) {
+  g_last_error[0] = '\0';
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "B, H, Nq, Nk must be >= 0");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d must be 64 or 128");
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (causal && Nq != Nk) return fail(FA_ERR_UNSUPPORTED, "causal masking needs Nq == Nk");
+  const int64_t bh = (int64_t)B * H;
+  if (bh > std::numeric_limits<int32_t>::max())
+    return fail(FA_ERR_UNSUPPORTED, "B*H exceeds int32");
+  if (bh == 0 || Nq == 0) return 1;
+  if (!q || !o || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "q, o and lse must be non-null");
+  if (Nk > 0 && (!k || !v)) return fail(FA_ERR_INVALID_ARGUMENT, "k and v must be non-null");
+  if (!aligned(q, 16) || !aligned(o, 16) || (k && !aligned(k, 16)) || (v && !aligned(v, 16)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "q, k, v and o must be 16-byte aligned");
+  if (!aligned(lse, 4) || (kv_seqlens && !aligned(kv_seqlens, 4)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "lse and kv_seqlens must be 4-byte aligned");
+  return FA_OK;
+}
+
+fa::PrefillParams prefill_params(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int B, int H, int Nq, int Nk, float scale, int causal,
+                                 const int32_t* kv_seqlens) {
+  fa::PrefillParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.kv_seqlens = kv_seqlens;
+  p.B = B;
+  p.H = H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.c = (float)((double)scale * 1.4426950408889634);  // scores in base-2 units
+  p.causal = causal;
+  return p;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                      const int32_t* kv_seqlens, void* stream) {
+  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (Nq == 1) {
+    if (B > 65535 || H > 65535) return fail(FA_ERR_UNSUPPORTED, "decode needs B, H <= 65535");
+    fa::DecodeParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.o = static_cast<uint16_t*>(o);
+    p.lse = lse;
+    p.kv_seqlens = kv_seqlens;
+    p.B = B;
+    p.H = H;
+    p.Nk = Nk;
+    p.c = (float)((double)scale * 1.4426950408889634);
+    const int chunk = fa::decode_chunk();
+    p.n_splits = (Nk + chunk - 1) / chunk;
+    const size_t n_part = (size_t)B * H * (size_t)p.n_splits;
+    void* ws = nullptr;
+    if (n_part > 0) {
+      hipError_t e = hipMallocAsync(&ws, n_part * (size_t)(d + 1) * sizeof(float), s);
+      if (e != hipSuccess) return fail_hip(e, "hipMallocAsync(decode workspace)");
+      p.ws_o = static_cast<float*>(ws);
+      p.ws_lse = p.ws_o + n_part * d;
+    }
+    hipError_t e = fa::launch_decode_bf16(p, d, s);
+    if (ws) {
+      hipError_t ef = hipFreeAsync(ws, s);
+      if (e == hipSuccess) e = ef;
+    }
+    if (e != hipSuccess) return fail_hip(e, "decode launch");
+    return FA_OK;
+  }
+
+  const int bm = fa::prefill_bf16_rows_per_wg(d);
+  const int64_t n_wg = (int64_t)B * H * ((Nq + bm - 1) / bm);
+  if (n_wg > std::numeric_limits<int32_t>::max()) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  fa::PrefillParams p = prefill_params(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_seqlens);
+  hipError_t e = fa::launch_prefill_bf16(p, d, s);
+  if (e != hipSuccess) return fail_hip(e, "prefill launch");
+  return FA_OK;
+}
+
+extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                          const int32_t* kv_seqlens, void* stream) {
+  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  const int64_t n_wg = (int64_t)B * H * ((Nq + 127) / 128);
+  if (n_wg > std::numeric_limits<int32_t>::max()) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  fa::PrefillParams p = prefill_params(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_seqlens);
+  hipError_t e = fa::launch_prefill_f32(p, d, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "prefill launch");
+  return FA_OK;
+}
+
+extern "C" const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_INVALID_ARGUMENT: return "FA_ERR_INVALID_ARGUMENT: an argument is out of range";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: valid but not supported by this library";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown fa status";
+  }
+}
+
+extern "C" const char* fa_last_error(void) { return g_last_error; }

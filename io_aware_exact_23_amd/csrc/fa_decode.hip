@@ -1,0 +1,199 @@
+// fa_decode.hip -- split-KV attention for one query per (b, h) (decode), bf16, gfx950.
+//
+// Decode is a separate phase that the pages ask to be measured apart from prefill (page
+// "FlashAttention：把注意力从公式写成数据流", section "评估清单"), and the vocus page names
+// FlashDecoding as its IO-aware form (section "結論"). With one query there is no reuse of K/V,
+// so the pass is bound by HBM bandwidth: every valid key is read exactly once.
+//
+// Kernel 1 (split): one workgroup per (chunk of kChunk keys, h, b). Each wave streams kChunk/4
+// keys with 16-byte loads, kLanesPerKey lanes per key row (whole rows per load instruction:
+// perfectly coalesced), forms the dot products on the vector ALUs, and keeps a local max, sum
+// and unnormalised output. The 4 waves merge through LDS into one partial (o_c, lse_c) per
+// chunk: o_c normalised, lse_c = log2 sum_j 2^(t_j) in base-2 units.
+// Kernel 2 (combine): per (b, h), lse* = max_c lse_c, w_c = 2^(lse_c - lse*),
+// O = sum w_c o_c / sum w_c, lse = ln 2 * (lse* + log2 sum w_c). Exact in exact arithmetic,
+// for any chunk size.
+#include "fa_device.h"
+#include "fa_params.h"
+
+namespace fa {
+
+constexpr int kDecodeChunk = 256;
+
+// Sum over aligned groups of N lanes (N a power of two <= 64).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < N; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+template <int D, int CHUNK>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void decode_split_kernel(DecodeParams p) {
+  constexpr int kLanesPerKey = D / 8;          // 16 bytes (8 bf16) per lane
+  constexpr int kKeysPerLoad = 64 / kLanesPerKey;
+  constexpr int kKeysPerWave = CHUNK / 4;
+  constexpr int kRounds = kKeysPerWave / kKeysPerLoad;
+  static_assert(kRounds * kKeysPerLoad == kKeysPerWave, "chunk must split evenly");
+
+  __shared__ float sm_m[4], sm_l[4];
+  __shared__ float sm_o[4][D];
+
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int L = seq_len(p.kv_seqlens, b, p.Nk);
+  const int key0 = split * CHUNK;
+  if (key0 >= L) return;  // the whole workgroup leaves together: no barrier is skipped
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int slot = lane / kLanesPerKey;  // which key of a load round
+  const int part = lane % kLanesPerKey;  // which 8-wide piece of d
+  const size_t bh = (size_t)b * p.H + h;
+
+  const u32x4 qx = *reinterpret_cast<const u32x4*>(p.q + bh * D + part * 8);
+  float qf[8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    qf[2 * t] = bf16_lo(qx[t]);
+    qf[2 * t + 1] = bf16_hi(qx[t]);
+  }
+
+  const uint16_t* Kb = p.k + bh * (size_t)p.Nk * D + part * 8;
+  const uint16_t* Vb = p.v + bh * (size_t)p.Nk * D + part * 8;
+  const int kw0 = key0 + w * kKeysPerWave + slot;
+
+  u32x4 kr[kRounds], vr[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int key = kw0 + r * kKeysPerLoad;
+    u32x4 z = {0u, 0u, 0u, 0u};
+    kr[r] = key < L ? *reinterpret_cast<const u32x4*>(Kb + (size_t)key * D) : z;
+  }
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int key = kw0 + r * kKeysPerLoad;
+    u32x4 z = {0u, 0u, 0u, 0u};
+    vr[r] = key < L ? *reinterpret_cast<const u32x4*>(Vb + (size_t)key * D) : z;
+  }
+
+  // Scores in base-2 units, t = c * q.k; keys past L get -inf.
+  float t[kRounds];
+  float mx = -kInf;
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    float dot = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dot = fmaf(qf[2 * e], bf16_lo(kr[r][e]), dot);
+      dot = fmaf(qf[2 * e + 1], bf16_hi(kr[r][e]), dot);
+    }
+    dot = group_sum<kLanesPerKey>(dot);
+    const int key = kw0 + r * kKeysPerLoad;
+    t[r] = key < L ? dot * p.c : -kInf;
+    mx = fmaxf(mx, t[r]);
+  }
+#pragma unroll
+  for (int m = kLanesPerKey; m < 64; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+
+  float lw = 0.0f;
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+  if (mx != -kInf) {
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const float pr = fast_exp2(t[r] - mx);  // 0 for masked keys
+      lw += pr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = fmaf(pr, bf16_lo(vr[r][e]), o[2 * e]);
+        o[2 * e + 1] = fmaf(pr, bf16_hi(vr[r][e]), o[2 * e + 1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = kLanesPerKey; m < 64; m <<= 1) {
+    lw += __shfl_xor(lw, m, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], m, 64);
+  }
+  if (slot == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm_o[w][part * 8 + e] = o[e];
+    if (part == 0) {
+      sm_m[w] = mx;
+      sm_l[w] = lw;
+    }
+  }
+  __syncthreads();
+
+  if (tid < D) {
+    float M = sm_m[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) M = fmaxf(M, sm_m[i]);
+    // M is finite: key0 < L, so wave 0 saw at least one valid key.
+    float lt = 0.0f, ot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f = sm_m[i] == -kInf ? 0.0f : fast_exp2(sm_m[i] - M);
+      lt = fmaf(sm_l[i], f, lt);
+      ot = fmaf(sm_o[i][tid], f, ot);
+    }
+    const size_t ws = bh * p.n_splits + split;
+    p.ws_o[ws * D + tid] = ot / lt;
+    if (tid == 0) p.ws_lse[ws] = M + fast_log2(lt);
+  }
+}
+
+template <int D, int CHUNK>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64)))
+void decode_combine_kernel(DecodeParams p) {
+  const int bh = blockIdx.x;
+  const int b = bh / p.H;
+  const int lane = threadIdx.x;
+  const int L = seq_len(p.kv_seqlens, b, p.Nk);
+  const int n = (L + CHUNK - 1) / CHUNK;
+  const float* lse_s = p.ws_lse + (size_t)bh * p.n_splits;
+  const float* o_s = p.ws_o + (size_t)bh * p.n_splits * D;
+
+  float M = -kInf;
+  for (int s = 0; s < n; ++s) M = fmaxf(M, lse_s[s]);
+  float W = 0.0f;
+  float acc[D / 64];
+#pragma unroll
+  for (int t = 0; t < D / 64; ++t) acc[t] = 0.0f;
+  for (int s = 0; s < n; ++s) {
+    const float wgt = fast_exp2(lse_s[s] - M);
+    W += wgt;
+#pragma unroll
+    for (int t = 0; t < D / 64; ++t) acc[t] = fmaf(wgt, o_s[(size_t)s * D + lane + 64 * t], acc[t]);
+  }
+  const float inv = n > 0 ? 1.0f / W : 0.0f;
+#pragma unroll
+  for (int t = 0; t < D / 64; ++t) {
+    const float x = acc[t] * inv;
+    p.o[(size_t)bh * D + lane + 64 * t] = (uint16_t)(pack_bf16(x, 0.0f) & 0xffffu);
+  }
+  if (lane == 0) p.lse[bh] = n > 0 ? (M + fast_log2(W)) * kLn2 : -kInf;
+}
+
+int decode_chunk() { return kDecodeChunk; }
+
+hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream) {
+  const dim3 grid1(p.n_splits, p.H, p.B);
+  const dim3 grid2(p.B * p.H);
+  if (d == 64) {
+    if (p.n_splits > 0) hipLaunchKernelGGL((decode_split_kernel<64, kDecodeChunk>), grid1, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_combine_kernel<64, kDecodeChunk>), grid2, dim3(64), 0, stream, p);
+  } else {
+    if (p.n_splits > 0) hipLaunchKernelGGL((decode_split_kernel<128, kDecodeChunk>), grid1, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_combine_kernel<128, kDecodeChunk>), grid2, dim3(64), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fa

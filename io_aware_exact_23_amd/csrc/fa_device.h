@@ -1,0 +1,77 @@
+// fa_device.h -- small device helpers shared by the libfa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kInf = __builtin_inff();
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Valid key count of sequence b: kv_seqlens[b] clamped to [0, Nk], or Nk without lengths.
+__device__ __forceinline__ int seq_len(const int32_t* lens, int b, int nk) {
+  return lens ? clampi(lens[b], 0, nk) : nk;
+}
+
+// 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) on the transcendental unit (v_log_f32).
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Cross-half combines over lanes l and l ^ 32 of the wave, on v_permlane32_swap (a VALU
+// exchange of the two 32-lane halves). The swap of (x, x) returns, in every lane, the pair
+// {own value, partner value} in some order, so a symmetric combine of the two results is
+// the combine over the lane pair.
+__device__ __forceinline__ float pair32_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_min(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Wave-uniform "any lane true".
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// bf16 <-> fp32. A bf16 value is the upper half of a binary32 value.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32). `a` lands in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 p = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// Workgroups of one launch are handed out round-robin over the 8 XCDs of the MI355X, and each
+// XCD has its own L2. Map hardware workgroup id -> logical tile so that every XCD receives one
+// contiguous range of logical tiles (tiles that share K/V then share an L2).
+__device__ __forceinline__ int xcd_remap(int wg, int n) {
+  constexpr int kXcd = 8;
+  const int xcd = wg % kXcd;
+  const int slot = wg / kXcd;
+  const int per = n / kXcd;
+  const int rem = n % kXcd;
+  return xcd * per + (xcd < rem ? xcd : rem) + slot;
+}
+
+}  // namespace fa

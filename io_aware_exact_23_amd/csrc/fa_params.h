@@ -1,0 +1,38 @@
+// fa_params.h -- plain argument blocks passed by value to the libfa kernels (host and device).
+#pragma once
+
+#include <stdint.h>
+
+namespace fa {
+
+// Tiled forward (prefill) kernels, bf16 and fp32. Element pointers are typed by the kernel.
+struct PrefillParams {
+  const void* q;  // [B][H][Nq][D]
+  const void* k;  // [B][H][Nk][D]
+  const void* v;  // [B][H][Nk][D]
+  void* o;        // [B][H][Nq][D]
+  float* lse;     // [B][H][Nq]
+  const int32_t* kv_seqlens;  // [B] or nullptr
+  int B, H, Nq, Nk;
+  float c;        // scale * log2(e): scores are handled in base-2 units
+  int causal;
+  int n_qtiles;   // ceil(Nq / BM)
+  int n_tiles;    // B * H * n_qtiles (the grid size)
+};
+
+// Split-KV decode (Nq == 1): one workgroup per (split, h, b), then a combine pass.
+struct DecodeParams {
+  const uint16_t* q;  // [B][H][1][D] bf16
+  const uint16_t* k;  // [B][H][Nk][D] bf16
+  const uint16_t* v;  // [B][H][Nk][D] bf16
+  uint16_t* o;        // [B][H][1][D] bf16
+  float* lse;         // [B][H]
+  const int32_t* kv_seqlens;
+  float* ws_o;        // [B][H][n_splits][D]  normalised partial outputs, fp32
+  float* ws_lse;      // [B][H][n_splits]     partial logsumexp in base-2 units
+  int B, H, Nk;
+  int n_splits;       // ceil(Nk / CHUNK)
+  float c;            // scale * log2(e)
+};
+
+}  // namespace fa

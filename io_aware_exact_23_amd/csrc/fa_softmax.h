@@ -1,0 +1,68 @@
+// fa_softmax.h -- the online-softmax update of one K/V tile for one query row.
+//
+// The method keeps, per query row, a running maximum, a running normaliser and an output
+// accumulator, and rescales the latter two whenever the maximum grows (page "FlashAttention 与
+// 边缘设备上的注意力内存瓶颈", section "3.2 Online Softmax"; page "FlashAttention：把注意力从公式
+// 写成数据流", section "分块与在线 softmax"). Here scores are kept in base-2 units: a raw dot
+// product s becomes t = c*s with c = scale*log2(e), and p = 2^(t - m) on v_exp_f32.
+//
+// Lazy rescaling. The offset m used for p need not be the exact running maximum: any offset
+// gives the same O = sum p v / sum p and lse = m + log2(sum p). The offset is raised only when a
+// tile's maximum exceeds it by more than kTau (so p <= 2^kTau stays far from fp32 overflow),
+// which skips the rescale of the output accumulator on almost every tile.
+#pragma once
+
+#include "fa_device.h"
+
+namespace fa {
+
+constexpr float kTau = 8.0f;
+
+// One query row is shared by the lane pair (l, l ^ 32); each lane holds NV scores of it.
+// On entry s[] holds raw dot products q.k; valid(i) tells whether score i's key is allowed
+// (only consulted when need_mask). On return s[] holds p (0 for masked keys), lsum includes
+// them, and the return value is the factor by which the caller must multiply its output
+// accumulator (1 when nothing changed); `rescaled` is wave-uniform.
+template <int NV, typename ValidFn>
+__device__ __forceinline__ float softmax_tile(float (&s)[NV], bool need_mask, ValidFn valid,
+                                              float c, bool neg, float& m_used, float& lsum,
+                                              bool& rescaled) {
+  // The row extreme of t = c*s is max(s)*c for c >= 0 and min(s)*c for c < 0; masked entries
+  // get the sentinel that can never be the extreme.
+  const float sentinel = neg ? kInf : -kInf;
+  if (need_mask) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) s[i] = valid(i) ? s[i] : sentinel;
+  }
+  float ext = s[0];
+  if (!neg) {
+#pragma unroll
+    for (int i = 1; i < NV; ++i) ext = fmaxf(ext, s[i]);
+    ext = pair32_max(ext);
+  } else {
+#pragma unroll
+    for (int i = 1; i < NV; ++i) ext = fminf(ext, s[i]);
+    ext = pair32_min(ext);
+  }
+  const float mt = (ext == sentinel) ? -kInf : ext * c;
+
+  float alpha = 1.0f;
+  rescaled = wave_any(mt > m_used + kTau);
+  if (rescaled) {
+    const float mn = fmaxf(m_used, mt);
+    alpha = (mn == -kInf) ? 1.0f : fast_exp2(m_used - mn);
+    m_used = mn;
+    lsum *= alpha;
+  }
+  const float moff = (m_used == -kInf) ? 0.0f : m_used;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float p = fast_exp2(fmaf(s[i], c, -moff));
+    if (need_mask) p = valid(i) ? p : 0.0f;
+    s[i] = p;
+    lsum += p;
+  }
+  return alpha;
+}
+
+}  // namespace fa

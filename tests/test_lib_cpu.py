@@ -1,0 +1,93 @@
+"""libfa on the CPU: the shared library loads, exports every symbol of include/fa.h, and rejects
+bad arguments before touching the GPU (no kernel is launched in this file)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import io_aware_exact_23_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(fa.library_path()),
+                               reason="libfa.so not built (run python -m io_aware_exact_23_amd.build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == ["fa_fwd", "fa_fwd_f32", "fa_last_error", "fa_status_string"]
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+@needs_lib
+def test_status_strings():
+    for st in (0, -1, -2, -3):
+        assert fa.fa_status_string(st).startswith(("FA_OK", "FA_ERR"))
+    assert fa.fa_status_string(7) == "unknown fa status"
+
+
+# Fake device addresses: argument checks must reject these calls before any HIP call.
+A = 0x10000000
+BAD = 0x10000001
+
+
+@needs_lib
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED, "64 or 128"),
+    (dict(d=0), fa.FA_ERR_UNSUPPORTED, "64 or 128"),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARGUMENT, ">= 0"),
+    (dict(Nk=-3), fa.FA_ERR_INVALID_ARGUMENT, ">= 0"),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARGUMENT, "finite"),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARGUMENT, "finite"),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARGUMENT, "causal"),
+    (dict(causal=1, Nq=4, Nk=5), fa.FA_ERR_UNSUPPORTED, "Nq == Nk"),
+    (dict(q=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(k=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(q=BAD), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(v=A + 8), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(lse=A + 2), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(kv_seqlens=A + 1), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(B=70000, H=70000), fa.FA_ERR_UNSUPPORTED, "int32"),
+])
+def test_argument_errors(fn, args, status, needle):
+    call = dict(q=A, k=A, v=A, o=A, lse=A, B=2, H=3, Nq=8, Nk=8, d=64, scale=0.125, causal=0,
+                kv_seqlens=None, stream=0)
+    call.update(args)
+    with pytest.raises(fa.FaError) as ei:
+        getattr(fa, fn)(**call)
+    assert ei.value.status == status
+    assert needle in ei.value.message
+
+
+@needs_lib
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+@pytest.mark.parametrize("args", [dict(B=0), dict(H=0), dict(Nq=0), dict(B=0, q=None, o=None, lse=None)])
+def test_empty_batch_is_a_no_op(fn, args):
+    call = dict(q=A, k=A, v=A, o=A, lse=A, B=2, H=3, Nq=8, Nk=8, d=128, scale=0.1, causal=0,
+                kv_seqlens=None, stream=0)
+    call.update(args)
+    getattr(fa, fn)(**call)  # returns FA_OK without launching anything
+    assert fa.fa_last_error() == ""
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "_lib", None)
+    monkeypatch.setattr(fa, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(fa.FaError):
+        fa.fa_status_string(0)

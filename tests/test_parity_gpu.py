@@ -1,0 +1,216 @@
+"""GPU parity: libfa (through its C ABI) against the fp64 oracle on the same input bits.
+
+Sizes span several tiles and ragged tails; the five named workloads run at full size (the
+16K causal prefill compares sampled rows, every head). Edge cases: single key, empty sequences,
+Nk == 0, poisoned padding, huge scores, negative and zero scale, bitwise repeatability, and
+decode (split-KV) against the tiled kernel.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_exact_23_amd as fa
+from io_aware_exact_23_amd import configs, inputs
+
+from parity_util import compare, run_lib, run_oracle, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load_library()  # raises if the HIP library is missing: no fallback exists
+
+
+def _rand(shape, seed, dtype, std=1.0):
+    return inputs.normal(shape, seed, DEV, dtype, std)
+
+
+def _case(B, H, Nq, Nk, d, dtype, causal, lens, seed, std=1.0, scale=None):
+    q = _rand((B, H, Nq, d), seed, dtype, std)
+    k = _rand((B, H, Nk, d), seed + 1, dtype, std)
+    v = _rand((B, H, Nk, d), seed + 2, dtype, std)
+    lt = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    if scale is None:
+        scale = d ** -0.5
+    return q, k, v, lt, scale
+
+
+def _check(q, k, v, lt, scale, causal, dtype, what):
+    o, lse = run_lib(q, k, v, scale, causal, lt)
+    o_ref, lse_ref = run_oracle(q, k, v, scale, causal, lt)
+    print(what, flush=True)
+    return compare(to_f64(o), to_f64(lse), o_ref, lse_ref, dtype, what=what)
+
+
+SMALL = [
+    # B, H, Nq, Nk, causal, lens
+    (1, 1, 17, 17, True, None),
+    (2, 3, 100, 300, False, None),
+    (1, 2, 129, 129, True, None),
+    (2, 2, 256, 256, True, [256, 77]),
+    (2, 1, 200, 333, False, [1, 333]),
+    (1, 1, 64, 64, False, None),
+    (3, 2, 300, 300, True, None),
+    (2, 2, 2, 65, False, [65, 3]),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,Nq,Nk,causal,lens", SMALL)
+def test_small_shapes(dtype, d, B, H, Nq, Nk, causal, lens):
+    q, k, v, lt, scale = _case(B, H, Nq, Nk, d, dtype, causal, lens, seed=Nq * 7 + Nk + d)
+    _check(q, k, v, lt, scale, causal, dtype, f"small {dtype} d={d} {B}x{H}x{Nq}x{Nk} causal={causal} lens={lens}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,Nk,lens", [(1, 1, 1, None), (2, 3, 700, [700, 1]), (3, 2, 513, [0, 256, 257]),
+                                          (4, 2, 8192, [8192, 1024, 4097, 5])])
+def test_decode_shapes(d, B, H, Nk, lens):
+    q, k, v, lt, scale = _case(B, H, 1, Nk, d, "bf16", False, lens, seed=Nk + d)
+    _check(q, k, v, lt, scale, False, "bf16", f"decode d={d} B={B} H={H} Nk={Nk} lens={lens}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_single_head_fp32_workload_and_dtypes(dtype):
+    w = configs.SINGLE_HEAD_FP32
+    q, k, v, _ = inputs.make(w, DEV)
+    if dtype == "bf16":
+        q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
+    _check(q, k, v, None, w.scale, w.causal, dtype, f"{w.name} as {dtype}")
+
+
+def test_gpt2_small_causal_workload():
+    w = configs.GPT2_SMALL_CAUSAL
+    q, k, v, lt = inputs.make(w, DEV)
+    _check(q, k, v, lt, w.scale, w.causal, "bf16", w.name)
+
+
+def test_bert_large_padded_workload():
+    w = configs.BERT_LARGE_PADDED
+    q, k, v, lt = inputs.make(w, DEV)
+    o, lse = run_lib(q, k, v, w.scale, w.causal, lt)
+    o_ref, lse_ref = run_oracle(q, k, v, w.scale, w.causal, lt)
+    lens = lt.cpu().numpy()
+    # Padded query rows (i >= L_b) are computed but not part of the result.
+    rows = np.arange(w.Nq)[None, None, :] < lens[:, None, None]
+    mask = np.broadcast_to(rows, lse_ref.shape)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, "bf16", row_mask=mask, what=w.name)
+
+
+def test_long_causal_16k_workload_sampled_rows():
+    w = configs.LONG_CAUSAL_16K
+    q, k, v, lt = inputs.make(w, DEV)
+    o, lse = run_lib(q, k, v, w.scale, w.causal, lt)
+    g = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(120, 136), g.integers(0, w.Nq, 40),
+                                     np.arange(w.Nq - 8, w.Nq)]))
+    o_ref, lse_ref = run_oracle(q, k, v, w.scale, w.causal, lt, rows=rows)
+    rows_t = torch.as_tensor(rows, device=DEV)
+    o_s = to_f64(o[:, :, rows_t])
+    lse_s = to_f64(lse[:, :, rows_t])
+    compare(o_s, lse_s, o_ref, lse_ref, "bf16", what=w.name + " sampled rows")
+    rel = np.linalg.norm(o_s - o_ref) / np.linalg.norm(o_ref)
+    assert rel < 1e-2, f"relative Frobenius error {rel:.3e}"
+    # Properties that hold at every row: finite output, lse between max score and max + ln(i+1).
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_decode_split_kv_workload():
+    w = configs.DECODE_SPLIT_KV
+    q, k, v, lt = inputs.make(w, DEV)
+    o, lse = run_lib(q, k, v, w.scale, w.causal, lt)
+    og, lg = to_f64(o), to_f64(lse)
+    for b0 in range(0, w.B, 8):
+        o_ref, lse_ref = run_oracle(q, k, v, w.scale, w.causal, lt, b_range=range(b0, b0 + 8))
+        compare(og[b0:b0 + 8], lg[b0:b0 + 8], o_ref, lse_ref, "bf16", what=f"{w.name} b{b0}")
+
+
+@pytest.mark.parametrize("Nq", [1, 200])
+def test_poisoned_padding_is_bit_identical(Nq):
+    B, H, Nk, d = 3, 2, 300, 128
+    lens = [300, 45, 129]
+    q, k, v, lt, scale = _case(B, H, Nq, Nk, d, "bf16", False, lens, seed=31)
+    kc, vc = k.clone(), v.clone()
+    inputs.fill_padding(kc, lt.cpu(), 0.0)
+    inputs.fill_padding(vc, lt.cpu(), 0.0)
+    kp, vp = k.clone(), v.clone()
+    inputs.fill_padding(kp, lt.cpu(), 1.0e4)
+    inputs.fill_padding(vp, lt.cpu(), float("nan"))
+    o1, l1 = run_lib(q, kc, vc, scale, False, lt)
+    o2, l2 = run_lib(q, kp, vp, scale, False, lt)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("Nq", [1, 1024])
+def test_bitwise_repeatable(Nq):
+    q, k, v, lt, scale = _case(2, 4, Nq, 1024, 128, "bf16", Nq > 1, None, seed=41)
+    o1, l1 = run_lib(q, k, v, scale, Nq > 1, lt)
+    o2, l2 = run_lib(q, k, v, scale, Nq > 1, lt)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_decode_matches_tiled_kernel():
+    # The same query twice (Nq = 2, non-causal) goes through the tiled kernel; Nq = 1 through the
+    # split-KV kernels. Both must agree to fp32 rounding plus one bf16 rounding of O.
+    B, H, Nk, d = 4, 3, 1500, 128
+    q, k, v, lt, scale = _case(B, H, 1, Nk, d, "bf16", False, [1500, 700, 1, 1025], seed=51)
+    o1, l1 = run_lib(q, k, v, scale, False, lt)
+    o2, l2 = run_lib(q.expand(B, H, 2, d).contiguous(), k, v, scale, False, lt)
+    assert torch.allclose(o1.float(), o2[:, :, :1].float(), atol=1.6e-2, rtol=0)
+    assert torch.allclose(o2[:, :, 0].float(), o2[:, :, 1].float(), atol=0, rtol=0)
+    assert torch.allclose(l1[:, :, 0], l2[:, :, 0], atol=1e-5, rtol=1e-6)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_huge_scores_stay_finite(dtype):
+    # Scores of magnitude ~1e2..1e3: naive exp in fp32 would overflow.
+    # fp32 dot products of magnitude ~1e3 carry absolute errors ~1e-4, which the softmax passes
+    # on to O; the 1e-5 fp32 bar does not apply to this stress case, the bf16 bar is used.
+    q, k, v, lt, _ = _case(2, 2, 150, 150, 64, dtype, True, None, seed=61, std=4.0)
+    _check(q, k, v, lt, 2.0, True, "bf16", f"huge scores {dtype}")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+@pytest.mark.parametrize("Nq", [1, 90])
+def test_negative_and_zero_scale(scale, Nq):
+    q, k, v, lt, _ = _case(2, 2, Nq, 190, 64, "bf16", False, [190, 60], seed=71)
+    _check(q, k, v, lt, scale, False, "bf16", f"scale={scale} Nq={Nq}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("Nq", [1, 40])
+def test_empty_sequences_and_no_keys(dtype, Nq):
+    if dtype == "fp32" and Nq == 1:
+        Nq = 3
+    q, k, v, lt, scale = _case(3, 2, Nq, 70, 128, dtype, False, [0, 1, 70], seed=81)
+    _check(q, k, v, lt, scale, False, dtype, f"empty/one-key sequences {dtype} Nq={Nq}")
+    # Nk == 0: every row has no allowed key.
+    k0 = torch.empty((3, 2, 0, 128), dtype=q.dtype, device=DEV)
+    o, lse = run_lib(q, k0, k0, scale, False, None)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_lengths_past_nk_are_clamped():
+    q, k, v, _, scale = _case(2, 1, 33, 50, 64, "bf16", False, None, seed=91)
+    big = torch.tensor([10_000, -5], dtype=torch.int32, device=DEV)
+    o, lse = run_lib(q, k, v, scale, False, big)
+    o_ref, lse_ref = run_oracle(q, k, v, scale, False, torch.tensor([50, 0], dtype=torch.int32))
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, "bf16", what="clamped lengths")
+
+
+def test_runs_on_a_side_stream():
+    q, k, v, lt, scale = _case(2, 2, 300, 300, 128, "bf16", True, None, seed=101)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = fa.attention(q, k, v, scale=scale, causal=True)
+    s.synchronize()
+    o_ref, lse_ref = run_oracle(q, k, v, scale, True, None)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, "bf16", what="side stream")
