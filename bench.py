@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward pass on one MI355X.
+
+A step is one fa_fwd call over one batch of synthetic input already resident in HBM. The
+default workload is the long-sequence causal prefill (B=2, H=16, N=16384, d=128, bf16); the
+decode workload (B=64, H=32, Nk=8192 cache with valid lengths in [1024, 8192], d=128) is timed in
+the same run and reported under "decode". Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode]
+                  [--no-cpu-baseline] [--cpu-seconds S] [--calibrate-copy]
+
+FLOPs are counted as 4*B*H*Nq*Nk*d, halved for causal masking. Decode bytes are the algorithmic
+HBM bytes: Q, the valid K and V rows, O and lse.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (bf16) and % of MFMA peak; decode HBM GB/s"
+PEAK_MFMA_BF16_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+KERNEL_SOURCES = ["fa_prefill_bf16.hip", "fa_decode.hip", "fa_device.h", "fa_softmax.h", "fa_params.h"]
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "io_aware_exact_23_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel: str, workload: str, sha: str):
+    """HBM bytes per launch from a committed counter summary, if taken on the current source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("RESULT "):
+                rec = json.loads(line[len("RESULT "):])
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, steps: int, warmup: int, torch):
+    """Run fn warmup times, then time `steps` calls with HIP events on the current stream.
+
+    Returns (total seconds over the timed region, list of per-launch seconds).
+    """
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total = t_start.elapsed_time(t_end) / 1e3
+    per = [s.elapsed_time(e) / 1e3 for s, e in zip(starts, ends)]
+    return total, per
+
+
+def cpu_baseline_prefill(w, q, k, v, seconds: float):
+    """The oracle, untuned, on a bounded sample of the workload.
+
+    Heads are taken in order (b, h) = (0, 0), (0, 1), ...; each head's query rows are visited in
+    16 interleaved passes (rows r, r+16, r+32, ...), so every pass has the same mix of causal
+    row lengths. Sampling stops after the first pass that ends past `seconds`.
+    """
+    import threadpoolctl
+    from oracle import attention_fwd
+
+    stride = 16
+    flops = 0
+    rows_done = 0
+    heads = []
+    t0 = time.perf_counter()
+    done = False
+    for b in range(w.B):
+        for h in range(w.H):
+            qh = q[b:b + 1, h:h + 1].float().cpu().double().numpy()
+            kh = k[b:b + 1, h:h + 1].float().cpu().double().numpy()
+            vh = v[b:b + 1, h:h + 1].float().cpu().double().numpy()
+            heads.append((b, h))
+            for start in range(stride):
+                rows = np.arange(start, w.Nq, stride)
+                attention_fwd(qh, kh, vh, w.scale, causal=w.causal, rows=rows)
+                # Same counting convention as the GPU: 4*d per (query, allowed key) pair.
+                n_keys = (rows + 1) if w.causal else np.full(len(rows), w.Nk)
+                flops += int(4 * w.d * n_keys.sum())
+                rows_done += len(rows)
+                if time.perf_counter() - t0 >= seconds:
+                    done = True
+                    break
+            if done:
+                break
+        if done:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_done} query rows ({len(heads)} heads, from (b, h) = (0, 0) in order) of "
+                      f"{w.name}, fp64 numpy with {threads} BLAS threads, {dt:.1f} s; FLOPs counted "
+                      f"as 4*d per (query row, allowed key)"}
+
+
+def decode_bytes(w, lens) -> int:
+    per_key = 2 * w.d * 2                      # one K row and one V row, bf16
+    per_bh = 2 * w.d * 2 + 4                   # Q and O rows (bf16) and lse (fp32)
+    return int(w.H * (per_key * int(lens.sum()) + per_bh * w.B))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_causal_b2_h16_n16384_d128")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported. "
+              "The kernels shard over (batch, head) with no communication; see the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import io_aware_exact_23_amd as fa
+    from io_aware_exact_23_amd import configs, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    fa.load_library()
+    dev = "cuda"
+    w = configs.BY_NAME[args.workload]
+    q, k, v, lens = inputs.make(w, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    fn_c = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
+
+    def step():
+        fn_c(q, k, v, o, lse, w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal), lens, None)
+
+    total, per = time_launches(step, args.steps, args.warmup, torch)
+    flops = w.counted_flops()
+    value = flops * args.steps / total / 1e12
+    avg_launch = float(np.mean(per))
+    achieved = flops / avg_launch / 1e12
+    sha = source_sha()
+    kernel = "prefill_bf16_kernel" if w.Nq > 1 else "decode_split_kernel"
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "input_std": w.input_std, "seed": w.seed,
+                   "counted_flops": flops},
+        "pct_mfma_peak": round(100.0 * value / PEAK_MFMA_BF16_TFLOPS, 2),
+        "roofline": {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4),
+                     "avg_launch_ms": round(avg_launch * 1e3, 4),
+                     "traffic": traffic_from_profile(kernel, w.name, sha),
+                     "source_sha": sha},
+    }
+
+    if not args.no_decode:
+        wd = configs.DECODE_SPLIT_KV
+        dq, dk, dv, dl = inputs.make(wd, dev)
+        do = torch.empty_like(dq)
+        dlse = torch.empty((wd.B, wd.H, 1), dtype=torch.float32, device=dev)
+
+        def dstep():
+            fa.fa_fwd(dq, dk, dv, do, dlse, wd.B, wd.H, 1, wd.Nk, wd.d, wd.scale, 0, dl, None)
+
+        dtotal, dper = time_launches(dstep, args.steps, args.warmup, torch)
+        nbytes = decode_bytes(wd, dl.cpu().numpy())
+        davg = float(np.mean(dper))
+        result["decode"] = {
+            "workload": wd.name, "unit": "GB/s",
+            "value": round(nbytes * args.steps / dtotal / 1e9, 1),
+            "ms_per_step": round(dtotal / args.steps * 1e3, 4),
+            "algorithmic_bytes": nbytes,
+            "pct_hbm_peak": round(100.0 * nbytes / davg / 1e9 / PEAK_HBM_GBS, 2),
+            "roofline": {"kernel": "decode_split_kernel + decode_combine_kernel (whole call)",
+                         "bound": "hbm", "achieved": round(nbytes / davg / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(nbytes / davg / 1e9 / PEAK_HBM_GBS, 4),
+                         "avg_launch_ms": round(davg * 1e3, 4),
+                         "traffic": traffic_from_profile("decode_split_kernel", wd.name, sha)},
+        }
+        del dq, dk, dv, do
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)  # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = src.numel() * 2
+
+    if not args.no_cpu_baseline and w.Nq > 1:
+        result["cpu_baseline"] = cpu_baseline_prefill(w, q, k, v, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

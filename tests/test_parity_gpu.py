@@ -174,7 +174,10 @@ def test_huge_scores_stay_finite(dtype):
     # Scores of magnitude ~1e2..1e3: naive exp in fp32 would overflow.
     # fp32 dot products of magnitude ~1e3 carry absolute errors ~1e-4, which the softmax passes
     # on to O; the 1e-5 fp32 bar does not apply to this stress case, the bf16 bar is used.
-    q, k, v, lt, _ = _case(2, 2, 150, 150, 64, dtype, True, None, seed=61, std=4.0)
+    # Only Q and K are scaled: V stays N(0, 1), as in every workload, so the absolute bar on O
+    # keeps its meaning (P is rounded to bf16 before P V; that error scales with |V|).
+    q, k, _, lt, _ = _case(2, 2, 150, 150, 64, dtype, True, None, seed=61, std=4.0)
+    v = _rand((2, 2, 150, 64), 64, dtype)
     _check(q, k, v, lt, 2.0, True, "bf16", f"huge scores {dtype}")
 
 
