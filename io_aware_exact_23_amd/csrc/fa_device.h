@@ -62,6 +62,31 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
+// Raw buffer resource over `bytes` bytes from `base`. Loads through it are range-checked by the
+// hardware: any 16-byte piece that does not lie inside [0, bytes) reads as zero, with no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds): lane i's bytes
+// land at lds_base + 16*i, and pieces outside the buffer's range are written as zeros.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, (int)byte_off, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes, lane 4a+b receives,
+// as its element j (j = 0..3), element b of the 4 consecutive 16-bit values addressed by lane
+// 4j+a of the group.
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
 // Workgroups of one launch are handed out round-robin over the 8 XCDs of the MI355X, and each
 // XCD has its own L2. Map hardware workgroup id -> logical tile so that every XCD receives one
 // contiguous range of logical tiles (tiles that share K/V then share an L2).

@@ -14,15 +14,21 @@
 //   * the probabilities are already in the B-operand layout of O^T += V^T * P^T, and the output
 //     accumulator O^T again has one query per lane, so the per-row rescale needs no shuffle.
 // The K rows fed to the A operand are permuted within each 32-key block (bits 2 and 3 of the row
-// index swapped) so that each lane's 16 scores are two runs of 8 consecutive keys; a run of 8
-// consecutive keys is exactly one 16-byte read of V^T from LDS.
+// index swapped) so that each lane's 16 scores are two runs of 8 consecutive keys, which is
+// exactly the key order the V^T operand wants.
 //
-// LDS per stage: K tile [BN][D + 8] (16-byte row padding) and V^T tile [D][BN] built by an
-// in-register 4x8 transpose at store time, its 16-byte units XOR-swizzled by row. Two stages:
-// tile j + 1 is fetched from HBM into registers while tile j is consumed from LDS.
+// Data movement. K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ... lds), with
+// no registers and no ALU work on the way; the buffer's range check turns keys past the
+// sequence length into zeros. Both tiles keep their natural row layout, with the 16-byte pieces
+// of each row XOR-swizzled against LDS bank conflicts; the V^T operand is read back transposed
+// with ds_read_b64_tr_b16. Two LDS stages, one per static array, so the compiler can see that the
+// loads into one stage never alias the reads of the other: tile j + 1 streams in while tile j is
+// consumed.
 #include "fa_device.h"
 #include "fa_params.h"
 #include "fa_softmax.h"
+
+#include <type_traits>
 
 namespace fa {
 
@@ -30,36 +36,33 @@ template <int D, int NQB>
 struct PrefillBf16Cfg {
   static constexpr int kWaves = 4;
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kQW = 32 * NQB;          // query rows per wave
-  static constexpr int kBM = kWaves * kQW;      // query rows per workgroup
-  static constexpr int kBN = 64;                // keys per K/V tile
-  static constexpr int kKStride = D + 8;        // bf16 per K row in LDS
-  static constexpr int kKElems = kBN * kKStride;
-  static constexpr int kVtElems = D * kBN;
-  static constexpr int kStageElems = kKElems + kVtElems;
-  static constexpr int kLdsBytes = 2 * kStageElems * 2;
-  static constexpr int kKChunks = kBN * D / 8 / kThreads;  // 16-byte K pieces per thread
-  static constexpr int kVJobs = (kBN / 4) * (D / 8);       // 4-key x 8-d V blocks per tile
-  static_assert(kKChunks * kThreads * 8 == kBN * D, "K tile must split evenly");
-  static_assert(kVJobs <= kThreads, "one V block per thread at most");
+  static constexpr int kQW = 32 * NQB;            // query rows per wave
+  static constexpr int kBM = kWaves * kQW;        // query rows per workgroup
+  static constexpr int kBN = 64;                  // keys per K/V tile
+  static constexpr int kNch = D / 8;              // 16-byte pieces per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = kBN * kRowBytes;
+  static constexpr int kStageBytes = 2 * kTileBytes;  // K tile, then V tile
+  static constexpr int kRowsPerKiB = 1024 / kRowBytes;
+  static constexpr int kKiBPerWave = kTileBytes / 1024 / kWaves;  // per tensor per tile
+  static_assert(kKiBPerWave * kWaves * 1024 == kTileBytes, "tile must split over the waves");
 };
 
-// Row of the K tile in LDS that holds key `r` (an involution: swap bits 2 and 3).
+// Row of the K tile in LDS that holds key `r` of the tile (an involution: swap bits 2 and 3).
 __device__ __forceinline__ int k_perm(int r) {
   return (r & ~0xC) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2);
 }
-// XOR swizzle of the 16-byte units (8 keys) of V^T row d.
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 
 template <int D, int NQB>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(PrefillParams p) {
   using C = PrefillBf16Cfg<D, NQB>;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  __shared__ __attribute__((aligned(1024))) char stage_a[C::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char stage_b[C::kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
@@ -78,6 +81,11 @@ void prefill_bf16_kernel(PrefillParams p) {
   const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + (size_t)bh * p.Nq * D;
   const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + (size_t)bh * p.Nk * D;
   const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + (size_t)bh * p.Nk * D;
+  // Range-checked views: rows >= Nq of Q and keys >= L of K and V read as zeros, so the loads
+  // need no branches and masked keys can never bring NaN or Inf into the products.
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, (uint32_t)p.Nq * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kg, (uint32_t)L * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vg, (uint32_t)L * C::kRowBytes);
 
   const int qw0 = q0 + w * C::kQW;
   const int qw_last = min(qw0 + C::kQW, p.Nq) - 1;  // < qw0 when the wave has no rows
@@ -88,13 +96,10 @@ void prefill_bf16_kernel(PrefillParams p) {
   bf16x8 qreg[NQB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    const int row = qw0 + qb * 32 + r32;
+    const uint32_t row = (uint32_t)(qw0 + qb * 32 + r32);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < p.Nq) x = *reinterpret_cast<const u32x4*>(Qg + (size_t)row * D + ks * 16 + g * 8);
-      qreg[qb][ks] = __builtin_bit_cast(bf16x8, x);
-    }
+    for (int ks = 0; ks < D / 16; ++ks)
+      qreg[qb][ks] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (row * D + ks * 16 + g * 8) * 2));
   }
 
   f32x16 oacc[NQB][D / 32];
@@ -109,159 +114,160 @@ void prefill_bf16_kernel(PrefillParams p) {
       for (int i = 0; i < 16; ++i) oacc[qb][db][i] = 0.0f;
   }
 
-  // K/V tile fetch (HBM -> registers) and store (registers -> LDS stage).
-  u32x4 kpre[C::kKChunks];
-  u32x4 vpre[4];
-  const int vc = tid % (D / 8);  // this thread's 8-wide d chunk of V
-  const int vkq = tid / (D / 8); // and its group of 4 keys
-
-  auto fetch = [&](int j) {
-    const int k0 = j * C::kBN;
+  // ---- HBM -> LDS. Wave w moves KiB blocks w*kKiBPerWave .. of each tile; in a block, lane i
+  // fills LDS row rb + i/kNch, 16-byte slot i%kNch. A K row r holds key k_perm(r) with piece
+  // (slot ^ (r % kNch)); a V row r holds key r with piece (slot ^ 4*(r % (kNch/4))).
+  uint32_t koff[C::kKiBPerWave], voff[C::kKiBPerWave];
 #pragma unroll
-    for (int it = 0; it < C::kKChunks; ++it) {
-      const int idx = tid + it * C::kThreads;
-      const int row = idx / (D / 8);
-      const int ch = idx % (D / 8);
-      const int key = k0 + row;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < L) x = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + ch * 8);
-      kpre[it] = x;
-    }
-    if (tid < C::kVJobs) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + vkq * 4 + r;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < L) x = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + vc * 8);
-        vpre[r] = x;
-      }
-    }
-  };
-
-  auto store = [&](int stage) {
-    uint16_t* Ks = smem + stage * C::kStageElems;
-    uint16_t* Vt = Ks + C::kKElems;
-#pragma unroll
-    for (int it = 0; it < C::kKChunks; ++it) {
-      const int idx = tid + it * C::kThreads;
-      const int row = idx / (D / 8);
-      const int ch = idx % (D / 8);
-      *reinterpret_cast<u32x4*>(Ks + k_perm(row) * C::kKStride + ch * 8) = kpre[it];
-    }
-    if (tid < C::kVJobs) {
-      const int unit = vkq >> 1;   // 8-key unit of the V^T row
-      const int half = vkq & 1;    // which 4 keys of the unit
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = vc * 8 + e;
-        const int wd = e >> 1;
-        uint32_t w01, w23;
-        if ((e & 1) == 0) {
-          w01 = (vpre[0][wd] & 0xffffu) | (vpre[1][wd] << 16);
-          w23 = (vpre[2][wd] & 0xffffu) | (vpre[3][wd] << 16);
-        } else {
-          w01 = (vpre[0][wd] >> 16) | (vpre[1][wd] & 0xffff0000u);
-          w23 = (vpre[2][wd] >> 16) | (vpre[3][wd] & 0xffff0000u);
-        }
-        u32x2 pr = {w01, w23};
-        *reinterpret_cast<u32x2*>(Vt + d * C::kBN + ((unit ^ vt_swz(d)) << 3) + half * 4) = pr;
-      }
-    }
-  };
-
-  if (ntiles > 0) {
-    fetch(0);
-    store(0);
+  for (int it = 0; it < C::kKiBPerWave; ++it) {
+    const int row = (w * C::kKiBPerWave + it) * C::kRowsPerKiB + lane / C::kNch;
+    const int slot = lane % C::kNch;
+    koff[it] = (uint32_t)(k_perm(row) * C::kRowBytes + ((slot ^ (row % C::kNch)) << 4));
+    voff[it] = (uint32_t)(row * C::kRowBytes + ((slot ^ (4 * (row % (C::kNch / 4)))) << 4));
   }
-  __syncthreads();
+  auto issue = [&](int j, char* stage) {
+    const uint32_t base = (uint32_t)j * C::kTileBytes;
+#pragma unroll
+    for (int it = 0; it < C::kKiBPerWave; ++it) {
+      char* blk = stage + (w * C::kKiBPerWave + it) * 1024;
+      buf_load16_lds(krs, blk, base + koff[it]);
+      buf_load16_lds(vrs, blk + C::kTileBytes, base + voff[it]);
+    }
+  };
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int st = j & 1;
-    if (j + 1 < ntiles) fetch(j + 1);
+  // ---- LDS -> operands (loop-invariant per-lane byte offsets).
+  // K A-operand: lane (r32, g) reads row kb*32 + r32, piece 2*ks + g.
+  const int krow_off = r32 * C::kRowBytes;
+  const int kx = r32 % C::kNch;
+  // V^T A-operand via transposed reads: in 16-lane group grp = lane/16 (gp = grp%2, g = grp/2),
+  // lane 4a+b addresses key (kb*32 + hh*16 + 8*g + 4*t + a), d = db*32 + 16*gp + 4*b.
+  const int li = lane & 15;
+  const int ta = li >> 2, tb = li & 3;
+  const int gp = (lane >> 4) & 1;
+  int vt_off[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int piece = db * 4 + 2 * gp + (tb >> 1);
+    const int sw = 4 * (ta % (C::kNch / 4));
+    vt_off[db] = (8 * g + ta) * C::kRowBytes + ((piece ^ sw) << 4) + 8 * (tb & 1);
+  }
 
-    const int k0 = j * C::kBN;
-    const bool active = (qw_last >= qw0) && (!p.causal || k0 <= qw_last);
-    if (active) {
-      const uint16_t* Ks = smem + st * C::kStageElems;
-      const uint16_t* Vt = Ks + C::kKElems;
+  // One K/V tile for this wave: scores, online softmax, output update. kMask selects the
+  // variant with per-element masks (tail tile, tiles crossing the wave's diagonal).
+  auto tile_step = [&](auto mask_tag, const char* stage, int k0) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    const char* Ks = stage;
+    const char* Vs = stage + C::kTileBytes;
 
-      // Scores: S^T[key][query] for the two 32-key blocks of the tile.
-      f32x16 sacc[NQB][2];
+    // Scores: S^T[key][query] for the two 32-key blocks of the tile.
+    f32x16 sacc[NQB][2];
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[qb][kb][i] = 0.0f;
+        for (int i = 0; i < 16; ++i) sacc[qb][kb][i] = 0.0f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint16_t* krow = Ks + (kb * 32 + r32) * C::kKStride + g * 8;
+    for (int kb = 0; kb < 2; ++kb) {
+      const char* krow = Ks + kb * 32 * C::kRowBytes + krow_off;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + ks * 16);
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (((2 * ks + g) ^ kx) << 4));
 #pragma unroll
-          for (int qb = 0; qb < NQB; ++qb)
-            sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], sacc[qb][kb], 0, 0, 0);
-        }
+        for (int qb = 0; qb < NQB; ++qb)
+          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], sacc[qb][kb], 0, 0, 0);
       }
+    }
 
-      // Masks are needed only on the tail tile and on tiles that cross this wave's diagonal.
-      const bool need_mask = (k0 + C::kBN > L) || (p.causal && k0 + C::kBN - 1 > qw0);
-
-      bf16x8 pk[NQB][2][2];
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 pk[NQB][2][2];
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int qi = qw0 + qb * 32 + r32;
-        float s[32];
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int qi = qw0 + qb * 32 + r32;
+      float s[32];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s[kb * 16 + i] = sacc[qb][kb][i];
-        // Score s[kb*16 + i] belongs to key k0 + kb*32 + 16*(i/8) + 8*g + i%8.
-        auto valid = [&](int x) {
-          const int kb = x >> 4, i = x & 15;
-          const int key = k0 + kb * 32 + ((i >> 3) << 4) + (g << 3) + (i & 7);
-          return key < L && (!p.causal || key <= qi);
-        };
-        bool rescaled;
-        const float alpha = softmax_tile<32>(s, need_mask, valid, c, neg, m_used[qb], lsum[qb], rescaled);
-        if (rescaled) {
+        for (int i = 0; i < 16; ++i) s[kb * 16 + i] = sacc[qb][kb][i];
+      // Score s[kb*16 + i] belongs to key k0 + 8*g + off(x) with the compile-time offset
+      // off(x) = kb*32 + 16*(i/8) + i%8; it is allowed iff off(x) < rem, where rem is this lane's
+      // count of allowed keys from k0 + 8*g on (keys < L, and keys <= qi when causal).
+      const int rem = (p.causal ? min(L, qi + 1) : L) - (k0 + 8 * g);
+      auto valid = [&](int x) {
+        const int kb = x >> 4, i = x & 15;
+        return kb * 32 + ((i >> 3) << 4) + (i & 7) < rem;
+      };
+      bool rescaled;
+      const float alpha = softmax_tile<32, kMask>(s, valid, c, neg, m_used[qb], lsum[qb], rescaled);
+      if (rescaled) {
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            u32x4 x;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-              x[t] = pack_bf16(s[kb * 16 + hh * 8 + 2 * t], s[kb * 16 + hh * 8 + 2 * t + 1]);
-            pk[qb][kb][hh] = __builtin_bit_cast(bf16x8, x);
-          }
+          for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
       }
-
-      // O^T[d][query] += V^T[d][keys] * P^T[keys][query], 16 keys per instruction.
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int unit = kb * 4 + hh * 2 + g;
+          u32x4 x;
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const int d = db * 32 + r32;
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vt + d * C::kBN + ((unit ^ vt_swz(d)) << 3));
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
-              oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[qb][kb][hh], oacc[qb][db], 0, 0, 0);
-          }
+          for (int t = 0; t < 4; ++t)
+            x[t] = pack_bf16(s[kb * 16 + hh * 8 + 2 * t], s[kb * 16 + hh * 8 + 2 * t + 1]);
+          pk[qb][kb][hh] = __builtin_bit_cast(bf16x8, x);
         }
     }
 
-    if (j + 1 < ntiles) store(st ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // O^T[d][query] += V^T[d][keys] * P^T[keys][query], 16 keys per instruction; the 8 keys of
+    // a lane's operand come from two transposed reads of 4 keys each.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const char* vrow = Vs + (kb * 32 + hh * 16) * C::kRowBytes;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const s16x4 lo = lds_read_tr16(vrow + vt_off[db]);
+          const s16x4 hi = lds_read_tr16(vrow + 4 * C::kRowBytes + vt_off[db]);
+          const s16x4 a8[2] = {lo, hi};
+          const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[qb][kb][hh], oacc[qb][db], 0, 0, 0);
+        }
+      }
+  };
+
+  // One iteration: start the next tile's loads into the other stage (free since the barrier
+  // that ended the previous iteration), consume this stage, then wait for the loads and meet.
+  auto iteration = [&](int j, const char* cur, char* nxt) {
+    if (j + 1 < ntiles) issue(j + 1, nxt);
+    const int k0 = j * C::kBN;
+    const bool active = (qw_last >= qw0) && (!p.causal || k0 <= qw_last);
+    if (active) {
+      // Masks are needed only on the tail tile and on tiles that cross this wave's diagonal.
+      const bool need_mask = (k0 + C::kBN > L) || (p.causal && k0 + C::kBN - 1 > qw0);
+      if (need_mask) tile_step(std::true_type{}, cur, k0);
+      else tile_step(std::false_type{}, cur, k0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads have landed in LDS
     __syncthreads();
+  };
+
+  // The Q loads must complete here, before the first tile's loads: the vector-memory counter is
+  // in order, so a Q load still pending inside the loop would make every wait for it also wait
+  // for the next tile's loads. The scheduling barriers keep the compiler from sinking them.
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+  if (ntiles > 0) {
+    issue(0, stage_a);
+    __builtin_amdgcn_s_waitcnt(0x3f70);
+  }
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    iteration(j, stage_a, stage_b);
+    if (j + 1 < ntiles) iteration(j + 1, stage_b, stage_a);
   }
 
   // Epilogue: O = O^T / l, lse = ln 2 * (m + log2 l); a row with no allowed key gets 0 and -inf.
@@ -290,18 +296,10 @@ void prefill_bf16_kernel(PrefillParams p) {
 template <int D, int NQB>
 static hipError_t launch_bf16(PrefillParams p, hipStream_t stream) {
   using C = PrefillBf16Cfg<D, NQB>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_bf16_kernel<D, NQB>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   p.n_qtiles = (p.Nq + C::kBM - 1) / C::kBM;
   p.n_tiles = p.B * p.H * p.n_qtiles;
   if (p.n_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NQB>), dim3(p.n_tiles), dim3(C::kThreads),
-                     C::kLdsBytes, stream, p);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NQB>), dim3(p.n_tiles), dim3(C::kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ void prefill_f32_kernel(PrefillParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
@@ -118,12 +118,13 @@ void prefill_f32_kernel(PrefillParams p) {
     float s[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = sacc[i];
-    auto valid = [&](int i) {
-      const int key = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
-      return key < L && (!p.causal || key <= qi);
-    };
+    // Score i belongs to key k0 + 4*g + 8*(i/4) + i%4; rem counts this lane's allowed keys from
+    // k0 + 4*g on (keys < L, and keys <= qi when causal).
+    const int rem = (p.causal ? min(L, qi + 1) : L) - (k0 + 4 * g);
+    auto valid = [&](int i) { return 8 * (i >> 2) + (i & 3) < rem; };
     bool rescaled;
-    const float alpha = softmax_tile<16>(s, need_mask, valid, c, neg, m_used, lsum, rescaled);
+    const float alpha = need_mask ? softmax_tile<16, true>(s, valid, c, neg, m_used, lsum, rescaled)
+                                  : softmax_tile<16, false>(s, valid, c, neg, m_used, lsum, rescaled);
     if (rescaled) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)

@@ -20,17 +20,17 @@ constexpr float kTau = 8.0f;
 
 // One query row is shared by the lane pair (l, l ^ 32); each lane holds NV scores of it.
 // On entry s[] holds raw dot products q.k; valid(i) tells whether score i's key is allowed
-// (only consulted when need_mask). On return s[] holds p (0 for masked keys), lsum includes
+// (only consulted when kMask). On return s[] holds p (0 for masked keys), lsum includes
 // them, and the return value is the factor by which the caller must multiply its output
 // accumulator (1 when nothing changed); `rescaled` is wave-uniform.
-template <int NV, typename ValidFn>
-__device__ __forceinline__ float softmax_tile(float (&s)[NV], bool need_mask, ValidFn valid,
+template <int NV, bool kMask, typename ValidFn>
+__device__ __forceinline__ float softmax_tile(float (&s)[NV], ValidFn valid,
                                               float c, bool neg, float& m_used, float& lsum,
                                               bool& rescaled) {
   // The row extreme of t = c*s is max(s)*c for c >= 0 and min(s)*c for c < 0; masked entries
   // get the sentinel that can never be the extreme.
   const float sentinel = neg ? kInf : -kInf;
-  if (need_mask) {
+  if constexpr (kMask) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) s[i] = valid(i) ? s[i] : sentinel;
   }
@@ -58,7 +58,9 @@ __device__ __forceinline__ float softmax_tile(float (&s)[NV], bool need_mask, Va
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     float p = fast_exp2(fmaf(s[i], c, -moff));
-    if (need_mask) p = valid(i) ? p : 0.0f;
+    // Allowed scores are finite, so the sentinel marks exactly the masked keys (this also covers
+    // c == 0, where the sentinel times c would give NaN).
+    if constexpr (kMask) p = (s[i] == sentinel) ? 0.0f : p;
     s[i] = p;
     lsum += p;
   }
