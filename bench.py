@@ -30,7 +30,9 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s (bf16) and % of MFMA peak; decode HBM GB/s"
 PEAK_MFMA_BF16_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
-KERNEL_SOURCES = ["fa_prefill_bf16.hip", "fa_decode.hip", "fa_device.h", "fa_softmax.h", "fa_params.h"]
+KERNEL_SOURCES = ["fa_prefill_bf16.hip", "fa_prefill_pp.hip", "fa_decode.hip", "fa_device.h", "fa_softmax.h",
+                  "fa_params.h", "fa_api.cpp"]
+LONG_NQ = 2048  # fa_fwd runs prefill_bf16_pp_kernel from this many query rows on
 
 
 def source_sha() -> str:
@@ -175,7 +177,10 @@ def main():
     avg_launch = float(np.mean(per))
     achieved = flops / avg_launch / 1e12
     sha = source_sha()
-    kernel = "prefill_bf16_kernel" if w.Nq > 1 else "decode_split_kernel"
+    if w.Nq == 1:
+        kernel = "decode_split_kernel"
+    else:
+        kernel = "prefill_bf16_pp_kernel" if w.Nq >= LONG_NQ else "prefill_bf16_kernel"
     result = {
         "metric": METRIC,
         "value": round(value, 2),

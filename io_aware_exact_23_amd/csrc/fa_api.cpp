@@ -11,9 +11,11 @@
 
 namespace fa {
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);
+hipError_t launch_prefill_bf16_pp(const PrefillParams& p, int d, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);
 int prefill_bf16_rows_per_wg(int d);
+constexpr int kPrefillLongNq = 2048;  // query rows from which the 8-wave prefill kernel is used
 int decode_chunk();
 }  // namespace fa
 
@@ -71,6 +73,10 @@ fa::PrefillParams prefill_params(const void* q, const void* k, const void* v, vo
   p.Nq = Nq;
   p.Nk = Nk;
   p.c = (float)((double)scale * 1.4426950408889634);  // scores in base-2 units
+  // A zero scale makes every allowed score 0. The kernels rely on c != 0 (a masked key's
+  // sentinel score times c must be -inf), so use a scale so small that every 2^(c*s) still rounds
+  // to exactly 1 and c*s is far below the resolution of the logsumexp: the results are those of c = 0.
+  if (p.c == 0.0f) p.c = 1e-30f;
   p.causal = causal;
   return p;
 }
@@ -121,7 +127,12 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   const int64_t n_wg = (int64_t)B * H * ((Nq + bm - 1) / bm);
   if (n_wg > std::numeric_limits<int32_t>::max()) return fail(FA_ERR_UNSUPPORTED, "grid too large");
   fa::PrefillParams p = prefill_params(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_seqlens);
-  hipError_t e = fa::launch_prefill_bf16(p, d, s);
+  // Long query sequences go to the 8-wave kernel that overlaps one wave's matrix work with its
+  // SIMD partner's softmax; its deeper pipeline and 256-row tiles pay off over many key tiles.
+  // Short sequences (few key tiles per workgroup, fewer workgroups) run faster on the 4-wave
+  // kernel with 128-row tiles.
+  hipError_t e = Nq >= fa::kPrefillLongNq ? fa::launch_prefill_bf16_pp(p, d, s)
+                                          : fa::launch_prefill_bf16(p, d, s);
   if (e != hipSuccess) return fail_hip(e, "prefill launch");
   return FA_OK;
 }

@@ -1,0 +1,444 @@
+// fa_prefill_pp.hip -- tiled attention forward for bf16 Q/K/V on gfx950 (MI355X), with the
+// matrix work of one wave overlapped against the softmax of its partner wave.
+//
+// What is computed is the tiled forward pass with an online softmax (page "FlashAttention：把注意
+// 力从公式写成数据流", sections "分块与在线 softmax" and "SRAM 预算与 tile 选择"; page
+// "FlashAttention 与边缘设备上的注意力内存瓶颈", sections "3.1 Tiling" and "3.2 Online Softmax"):
+// each query row keeps a running maximum, a running normaliser and an output accumulator in
+// registers while the K/V tiles of its head stream through LDS.
+//
+// Why two wave groups. On gfx950 a wave that interleaves v_exp_f32 with matrix instructions gets
+// no overlap between them, while the exponentials of one wave and the matrix instructions of
+// another wave on the same SIMD do overlap. So a workgroup holds 8 waves (2 per SIMD) in two
+// groups of 4, and the groups alternate between two kinds of phase, separated by workgroup
+// barriers:
+//   matrix phase i:  S_i = K_i Q^T (scores of key tile i) and O^T += V_{i-1}^T P_{i-1}^T
+//   softmax phase i: running max / normaliser update, P_i = 2^(t - m) as bf16, O rescale
+// Group 1 runs one phase behind group 0, so in every phase each SIMD has one wave on the matrix
+// cores and one on the vector ALUs. (This is the scheduling idea the pages credit to FA3 for
+// Hopper, page "FlashAttention：把注意力从公式写成数据流", section "FA2 与 FA3", rebuilt with
+// workgroup barriers and per-SIMD wave pairs instead of warp specialisation.)
+//
+// Matrix-core mapping (v_mfma_f32_32x32x16_bf16, fp32 accumulation). Each wave owns 32 query rows
+// and computes the TRANSPOSED score tile S^T = K Q^T, so every lane holds scores of ONE query
+// (lane % 32): the softmax row reductions are in-lane plus one cross-half exchange, the
+// probabilities are already the B operand of O^T += V^T P^T, and O^T again has one query per lane.
+// K rows are permuted inside each 32-key block (bits 2 and 3 swapped) so that a lane's 16 scores
+// of a block are two runs of 8 consecutive keys, the key order the V^T operand wants.
+//
+// Data movement. A pipeline unit U_i = (K tile i, V tile i-1) is consumed in the two phases
+// 2i, 2i+1 of the workgroup timeline. Four LDS slots hold U_i .. U_{i+3}; every wave copies its
+// 1/8 share of each unit from HBM straight into LDS (buffer_load_dwordx4 ... lds, no registers,
+// range-checked so keys past the workgroup's range read as zeros) about three phases before it
+// is needed. V^T operands come from transposing LDS reads (ds_read_b64_tr_b16).
+#include "fa_device.h"
+#include "fa_params.h"
+#include "fa_softmax.h"
+
+#include <type_traits>
+
+namespace fa {
+
+template <int D>
+struct PrefillPPCfg {
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kQW = 32;                  // query rows per wave
+  static constexpr int kBM = kWaves * kQW;        // query rows per workgroup
+  static constexpr int kBN = 64;                  // keys per K/V tile
+  static constexpr int kNch = D / 8;              // 16-byte pieces per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = kBN * kRowBytes;
+  static constexpr int kUnitBytes = 2 * kTileBytes;  // K tile, then V tile
+  static constexpr int kRowsPerKiB = 1024 / kRowBytes;
+  static constexpr int kKiBPerWave = kTileBytes / 1024 / kWaves;  // per tensor per tile
+  static constexpr int kLoadsPerUnit = 2 * kKiBPerWave;           // per wave
+  static_assert(kKiBPerWave * kWaves * 1024 == kTileBytes, "tile must split over the waves");
+};
+
+// Row of the K tile in LDS that holds key `r` of the tile (an involution: swap bits 2 and 3).
+__device__ __forceinline__ int pp_k_perm(int r) {
+  return (r & ~0xC) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void prefill_bf16_pp_kernel(PrefillParams p) {
+  using C = PrefillPPCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char slot0[C::kUnitBytes];
+  __shared__ __attribute__((aligned(1024))) char slot1[C::kUnitBytes];
+  __shared__ __attribute__((aligned(1024))) char slot2[C::kUnitBytes];
+  __shared__ __attribute__((aligned(1024))) char slot3[C::kUnitBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
+  const int grp = w >> 2;                                  // waves w and w + 4 share a SIMD
+  const int rblk = 2 * (w & 3) + grp;                      // the wave's 32-row block
+  const int r32 = lane & 31;
+  const int g = lane >> 5;
+
+  // Work decomposition: workgroup -> (b, h, query tile); causal tiles heaviest first.
+  const int tile = xcd_remap(blockIdx.x, p.n_tiles);
+  const int bh = tile / p.n_qtiles;
+  int qt = tile - bh * p.n_qtiles;
+  if (p.causal) qt = p.n_qtiles - 1 - qt;
+  const int b = bh / p.H;
+  const int q0 = qt * C::kBM;
+  const int L = seq_len(p.kv_seqlens, b, p.Nk);
+  int kend = L;
+  if (p.causal) kend = min(kend, min(q0 + C::kBM, p.Nq));
+  const int n = kend > 0 ? (kend + C::kBN - 1) / C::kBN : 0;  // key tiles of this workgroup
+
+  const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + (size_t)bh * p.Nq * D;
+  const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + (size_t)bh * p.Nk * D;
+  const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + (size_t)bh * p.Nk * D;
+  // Range-checked views: rows >= Nq of Q and keys >= kend of K and V read as zeros, so the loads
+  // need no branches, masked keys can never bring NaN or Inf into the products, and tiles past
+  // this workgroup's last one cost no memory traffic.
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, (uint32_t)p.Nq * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kg, (uint32_t)kend * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vg, (uint32_t)kend * C::kRowBytes);
+
+  const int qw0 = q0 + rblk * C::kQW;
+  const int qw_last = min(qw0 + C::kQW, p.Nq) - 1;  // < qw0 when the wave has no rows
+  // Scores are handled in base-2 units t = c * (q.k). For c < 0 the kernel negates its copy of Q
+  // (a sign flip, exact in bf16 and in every product and sum) and uses -c, so below c > 0 always
+  // and the running extreme is always a maximum.
+  const bool neg = p.c < 0.0f;
+  const float c = neg ? -p.c : p.c;
+
+  // Q rows -> registers, already in the B-operand layout of S^T = K Q^T.
+  bf16x8 qreg[D / 16];
+  {
+    const uint32_t row = (uint32_t)(qw0 + r32);
+    const uint32_t flip = neg ? 0x80008000u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 x = buf_load16(qrs, (row * D + ks * 16 + g * 8) * 2);
+      x ^= flip;
+      qreg[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.0f;
+  float m_used = -kInf, lsum = 0.0f;
+
+  // ---- HBM -> LDS. Wave w moves KiB blocks w*kKiBPerWave .. of each tile; in a block, lane i
+  // fills LDS row rb + i/kNch, 16-byte slot i%kNch. A K row r holds key pp_k_perm(r) with piece
+  // (slot ^ (r % kNch)); a V row r holds key r with piece (slot ^ 4*(r % (kNch/4))).
+  uint32_t koff[C::kKiBPerWave], voff[C::kKiBPerWave];
+#pragma unroll
+  for (int it = 0; it < C::kKiBPerWave; ++it) {
+    const int row = (w * C::kKiBPerWave + it) * C::kRowsPerKiB + lane / C::kNch;
+    const int slot = lane % C::kNch;
+    koff[it] = (uint32_t)(pp_k_perm(row) * C::kRowBytes + ((slot ^ (row % C::kNch)) << 4));
+    voff[it] = (uint32_t)(row * C::kRowBytes + ((slot ^ (4 * (row % (C::kNch / 4)))) << 4));
+  }
+  // Unit u = (K tile u, V tile u - 1). V tile -1 and K tile n lie outside the buffer range and
+  // read as zeros (the unsigned offset of tile -1 wraps far past any valid range).
+  auto issue_unit = [&](int u, char* dst) __attribute__((always_inline)) {
+    const uint32_t kbase = (uint32_t)u * C::kTileBytes;
+    const uint32_t vbase = (uint32_t)(u - 1) * C::kTileBytes;
+#pragma unroll
+    for (int it = 0; it < C::kKiBPerWave; ++it) {
+      char* blk = dst + (w * C::kKiBPerWave + it) * 1024;
+      buf_load16_lds(krs, blk, kbase + koff[it]);
+      buf_load16_lds(vrs, blk + C::kTileBytes, vbase + voff[it]);
+    }
+  };
+
+  // ---- LDS -> operands (loop-invariant per-lane byte offsets).
+  // K A-operand: lane (r32, g) reads row kb*32 + r32, piece 2*ks + g.
+  const int krow_off = r32 * C::kRowBytes;
+  const int kx = r32 % C::kNch;
+  // V^T A-operand via transposed reads: in 16-lane group grp16 = lane/16 (gp = grp16%2,
+  // g = grp16/2), lane 4a+b addresses key (kb*32 + hh*16 + 8*g + 4*t + a), d = db*32 + 16*gp + 4*b.
+  const int li = lane & 15;
+  const int ta = li >> 2, tb = li & 3;
+  const int gp = (lane >> 4) & 1;
+  int vt_off[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int piece = db * 4 + 2 * gp + (tb >> 1);
+    const int sw = 4 * (ta % (C::kNch / 4));
+    vt_off[db] = (8 * g + ta) * C::kRowBytes + ((piece ^ sw) << 4) + 8 * (tb & 1);
+  }
+
+  f32x16 sacc[2];   // S^T of key tile i (two 32-key blocks), then t = c*s - m in place, then p
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[kb][e] = -kInf;
+  bf16x8 pk[2][2];  // P^T of the previous key tile as bf16 B operands (zero before tile 0)
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) pk[kb][hh] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  bool rescale_pending = false;  // wave-uniform: O must be multiplied by alpha_pending before PV
+  float alpha_pending = 1.0f;
+
+  // ---- Matrix phase i: S_i = K_i Q^T, then O^T += V_{i-1}^T P_{i-1}^T, each a software-
+  // pipelined sequence of MFMAs whose LDS operand is read kAhead instructions before the MFMA
+  // that consumes it. While the PV MFMAs run, the same wave does the softmax bookkeeping of
+  // tile i on the vector ALUs (running max, rescale decision, exponent arguments), which this
+  // chip overlaps with the wave's own matrix instructions; only the exponentials, which it does
+  // not overlap, are left for the next phase.
+  // Every iteration runs the same code; the edges are handled by data instead of branches (a
+  // branch would make the compiler copy the accumulators at every join): unit 0 carries V tile
+  // -1 and unit n carries K tile n, both outside the buffer range and read as zeros; P before
+  // tile 0 is zero; and a tile with no allowed key for this wave (tile n, tiles past the wave's
+  // causal diagonal, rows past Nq) is fully masked, so its P is exactly zero.
+  constexpr int kAhead = 4;
+  constexpr int kNS = 2 * (D / 16);  // S MFMAs: key block kb = m % 2, d step ks = m / 2
+  constexpr int kNP = 4 * (D / 32);  // PV MFMAs: d block db = m % (D/32), key step u = m / (D/32)
+  constexpr int kNM = kNS + kNP;
+
+  // Running-max update for tile i on the scores in sacc; leaves the base-2 exponent arguments
+  // t = c*s - m in sacc. With kMask, keys this lane may not see (key k0 + 8*g + off with
+  // off = kb*32 + 16*(e/8) + e%8 allowed iff off < rem; rem counts the allowed keys from
+  // k0 + 8*g on: keys < L, keys <= qi when causal, none for rows past Nq) first get -inf, which c
+  // (> 0 here) keeps at t = -inf, so their p is exactly 0. Branch-free, so it shares a basic
+  // block with the matrix instructions.
+  auto update_max = [&](auto mask_tag, int k0) __attribute__((always_inline)) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    float s[32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb * 16 + e] = sacc[kb][e];
+    if constexpr (kMask) {
+      const int qi = qw0 + r32;
+      int rem = (p.causal ? min(L, qi + 1) : L) - (k0 + 8 * g);
+      if (qi >= p.Nq) rem = 0;
+#pragma unroll
+      for (int x = 0; x < 32; ++x) {
+        const int kb = x >> 4, e = x & 15;
+        s[x] = (kb * 32 + ((e >> 3) << 4) + (e & 7) < rem) ? s[x] : -kInf;
+      }
+    }
+    const float ext = pair32_max(tree_max(s));  // the row maximum of t = c*s is max(s)*c
+    const float mt = ext * c;                   // -inf when the whole row is masked
+    // Lazy rescaling: the offset moves only when the tile's maximum passes it by more than kTau.
+    const bool rescaled = wave_any(mt > m_used + kTau);
+    const float mn = rescaled ? fmaxf(m_used, mt) : m_used;
+    const float alpha = (rescaled && m_used != -kInf) ? fast_exp2(m_used - mn) : 1.0f;
+    rescale_pending = rescaled;
+    alpha_pending = alpha;
+    lsum *= alpha;
+    m_used = mn;
+    const float moff = (m_used == -kInf) ? 0.0f : m_used;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = fmaf(s[kb * 16 + e], c, -moff);
+  };
+
+  // ---- Matrix phase i: one software-pipelined sequence of kNM MFMAs, S_i = K_i Q^T and then
+  // O^T += V_{i-1}^T P_{i-1}^T, whose LDS operand m is read kAhead instructions before the MFMA
+  // that consumes it; the V reads start while the last S MFMAs run, so the phase pays the LDS
+  // latency once. Nothing else runs in this phase: a wave issues vector instructions slowly on
+  // its own, and each one it slots between its MFMAs delays the next MFMA.
+  // Every interval runs this same code; the edges are handled by data instead of branches (a
+  // branch would make the compiler copy the accumulators at every join): unit 0 carries V tile
+  // -1 and unit n carries K tile n, both outside the buffer range and read as zeros; P before
+  // tile 0 is zero; and a tile with no allowed key for this wave (tile n, tiles past the wave's
+  // causal diagonal, rows past Nq) is fully masked, so its P is exactly zero.
+  auto matrix_phase = [&](const char* unit) __attribute__((always_inline)) {
+    const char* Vs = unit + C::kTileBytes;
+    auto fetch = [&](int m) -> bf16x8 __attribute__((always_inline)) {
+      if (m < kNS) {
+        const int kb = m & 1, ks = m >> 1;
+        const char* krow = unit + kb * 32 * C::kRowBytes + krow_off;
+        return *reinterpret_cast<const bf16x8*>(krow + (((2 * ks + g) ^ kx) << 4));
+      }
+      const int mp = m - kNS;
+      const int db = mp % (D / 32), u = mp / (D / 32);
+      const char* vrow = Vs + u * 16 * C::kRowBytes + vt_off[db];
+      const s16x4 a8[2] = {lds_read_tr16(vrow), lds_read_tr16(vrow + 4 * C::kRowBytes)};
+      return __builtin_bit_cast(bf16x8, a8);
+    };
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.0f;
+    bf16x8 op[kNM];
+#pragma unroll
+    for (int m = 0; m < kAhead; ++m) op[m] = fetch(m);
+#pragma unroll
+    for (int m = 0; m < kNM; ++m) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (m + kAhead < kNM) op[m + kAhead] = fetch(m + kAhead);
+      if (m < kNS) {
+        sacc[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], qreg[m >> 1], sacc[m & 1], 0, 0, 0);
+      } else {
+        const int mp = m - kNS;
+        const int db = mp % (D / 32), u = mp / (D / 32);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], pk[u >> 1][u & 1], oacc[db], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Keep the softmax work of the other phase from being scheduled into this one.
+    asm volatile("" : "+v"(sacc[0]), "+v"(sacc[1]));
+  };
+
+  // Keep the exponentials next to the rest of the softmax work (without this the compiler sinks
+  // them to their use in the next PV matrix instructions, where this chip serialises them with the
+  // wave's MFMAs).
+  auto pin_softmax = [&]() __attribute__((always_inline)) {
+    asm volatile("" : "+v"(pk[0][0]), "+v"(pk[0][1]), "+v"(pk[1][0]), "+v"(pk[1][1]), "+v"(lsum),
+                 "+v"(m_used));
+  };
+  // ---- Softmax phase for the tile whose scores sit in sacc (key k0 onwards): running max and
+  // rescale decision (update_max), the rescale of O decided there (after the PV of the previous
+  // tile, before the PV of this one), p = 2^t, P -> bf16 B operands, row sums.
+  auto softmax_phase = [&](auto mask_tag, int k0) __attribute__((always_inline)) {
+    update_max(mask_tag, k0);
+    if (rescale_pending) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha_pending;
+    }
+    float pr[32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pr[kb * 16 + e] = fast_exp2(sacc[kb][e]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x4 x;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          x[t] = pack_bf16(pr[kb * 16 + hh * 8 + 2 * t], pr[kb * 16 + hh * 8 + 2 * t + 1]);
+        pk[kb][hh] = __builtin_bit_cast(bf16x8, x);
+      }
+    lsum += tree_sum(pr);
+    pin_softmax();
+  };
+
+  // One barrier interval i per key tile. Every wave issues its share of U_{i+3} into `ahead`, the
+  // slot that held U_{i-1} (consumed by both groups before the last barrier), outside its matrix
+  // phase. Group 0 runs matrix phase i (S_i, PV_{i-1}) and then the softmax of tile i; group 1
+  // runs the softmax of tile i-1 and then matrix phase i. So while a wave of one group works on the vector ALUs the
+  // wave of the other group on its SIMD issues matrix instructions. Before the barrier, this
+  // wave's share of U_{i+1} must have landed; U_{i+2} and U_{i+3} may still be in flight (loads
+  // get three intervals). kMask selects the masked softmax (group 1 applies it to tile i-1).
+  auto interval = [&](auto order_tag, auto mask_tag, int i, const char* unit, char* ahead)
+      __attribute__((always_inline)) {
+    constexpr bool kMatrixFirst = decltype(order_tag)::value;
+    if constexpr (kMatrixFirst) {
+      matrix_phase(unit);
+      issue_unit(i + 3, ahead);
+      softmax_phase(mask_tag, i * C::kBN);
+    } else {
+      issue_unit(i + 3, ahead);
+      softmax_phase(mask_tag, (i - 1) * C::kBN);
+      matrix_phase(unit);
+    }
+    wait_vmcnt<2 * C::kLoadsPerUnit>();
+    wg_barrier();
+  };
+  // Two loops, each with a single code path (a branch per tile would make the compiler copy the
+  // accumulators at every join): tiles 0 .. i_mask-1 need no mask for any wave of the workgroup;
+  // tiles i_mask .. n take the masked variant, a no-op mask on tiles that happen to be whole.
+  // Tiles needing a mask: the ragged tail (key k0 + 63 >= L), and when causal those reaching past
+  // the workgroup's first row (k0 + 63 > q0); tile n is fully masked. i_mask is rounded down to
+  // a multiple of the slot count, so both loops start on slot 0. Both loops are unrolled by the
+  // slot count so every LDS access names its slot array; the guards are nested so that the
+  // compiler's wait-count tracking sees only the paths that can happen.
+  int i_mask = min(n, L / C::kBN);
+  if (p.causal) i_mask = min(i_mask, q0 / C::kBN);
+  i_mask &= ~3;
+  auto run = [&](auto order_tag) __attribute__((always_inline)) {
+    int i = 0;
+    for (; i < i_mask; i += 4) {
+      interval(order_tag, std::false_type{}, i, slot0, slot3);
+      interval(order_tag, std::false_type{}, i + 1, slot1, slot0);
+      interval(order_tag, std::false_type{}, i + 2, slot2, slot1);
+      interval(order_tag, std::false_type{}, i + 3, slot3, slot2);
+    }
+    for (; i <= n; i += 4) {
+      interval(order_tag, std::true_type{}, i, slot0, slot3);
+      if (i + 1 <= n) {
+        interval(order_tag, std::true_type{}, i + 1, slot1, slot0);
+        if (i + 2 <= n) {
+          interval(order_tag, std::true_type{}, i + 2, slot2, slot1);
+          if (i + 3 <= n) interval(order_tag, std::true_type{}, i + 3, slot3, slot2);
+        }
+      }
+    }
+  };
+
+  // Prologue: Q and units 0, 1, 2 complete before anyone starts. Units past n (issued by the
+  // last intervals) fall outside the buffer range and only write zeros into free slots.
+  issue_unit(0, slot0);
+  issue_unit(1, slot1);
+  issue_unit(2, slot2);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<0>();
+  wg_barrier();
+  // Group 1's first exponential phase (of "tile -1") sees t = -inf everywhere: p = 0, no effect.
+  // After the last interval group 1 leaves tile n's exponentials undone; that tile is fully
+  // masked, so they would add nothing.
+  if (grp == 0) run(std::true_type{});
+  else run(std::false_type{});
+  wait_vmcnt<0>();  // nothing may still write into LDS when the workgroup ends
+
+  // Epilogue: O = O^T / l, lse = ln 2 * (m + log2 l); a row with no allowed key gets 0 and -inf.
+  uint16_t* Og = static_cast<uint16_t*>(p.o) + (size_t)bh * p.Nq * D;
+  float* lseg = p.lse + (size_t)bh * p.Nq;
+  const float lt = pair32_sum(lsum);
+  const int qi = qw0 + r32;
+  if (qi < p.Nq) {
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    if (g == 0) lseg[qi] = lt > 0.0f ? (m_used + fast_log2(lt)) * kLn2 : -kInf;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        // Accumulator entries 4*jq .. 4*jq+3 are d = db*32 + 8*jq + 4*g + 0..3 of row qi.
+        u32x2 x = {pack_bf16(oacc[db][4 * jq + 0] * inv, oacc[db][4 * jq + 1] * inv),
+                   pack_bf16(oacc[db][4 * jq + 2] * inv, oacc[db][4 * jq + 3] * inv)};
+        *reinterpret_cast<u32x2*>(Og + (size_t)qi * D + db * 32 + 8 * jq + 4 * g) = x;
+      }
+  }
+}
+
+template <int D>
+static hipError_t launch_pp(PrefillParams p, hipStream_t stream) {
+  using C = PrefillPPCfg<D>;
+  p.n_qtiles = (p.Nq + C::kBM - 1) / C::kBM;
+  p.n_tiles = p.B * p.H * p.n_qtiles;
+  if (p.n_tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((prefill_bf16_pp_kernel<D>), dim3(p.n_tiles), dim3(C::kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+int prefill_bf16_pp_rows_per_wg() { return PrefillPPCfg<128>::kBM; }
+
+hipError_t launch_prefill_bf16_pp(const PrefillParams& p, int d, hipStream_t stream) {
+  if (d == 64) return launch_pp<64>(p, stream);
+  return launch_pp<128>(p, stream);
+}
+
+}  // namespace fa

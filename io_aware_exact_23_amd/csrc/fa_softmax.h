@@ -18,6 +18,51 @@ namespace fa {
 
 constexpr float kTau = 8.0f;
 
+// Reductions over a lane's scores written as balanced trees (three-input max/min steps, pairwise
+// sums), so a wave running them alone is not held up by one long chain of dependent instructions.
+template <int N>
+__device__ __forceinline__ float tree_max(const float (&x)[N]) {
+  if constexpr (N == 1) {
+    return x[0];
+  } else {
+    constexpr int M = (N + 2) / 3;
+    float y[M];
+#pragma unroll
+    for (int k = 0; k < M; ++k) {
+      const int a = 3 * k;
+      y[k] = a + 2 < N ? fmaxf(fmaxf(x[a], x[a + 1]), x[a + 2]) : (a + 1 < N ? fmaxf(x[a], x[a + 1]) : x[a]);
+    }
+    return tree_max<M>(y);
+  }
+}
+template <int N>
+__device__ __forceinline__ float tree_min(const float (&x)[N]) {
+  if constexpr (N == 1) {
+    return x[0];
+  } else {
+    constexpr int M = (N + 2) / 3;
+    float y[M];
+#pragma unroll
+    for (int k = 0; k < M; ++k) {
+      const int a = 3 * k;
+      y[k] = a + 2 < N ? fminf(fminf(x[a], x[a + 1]), x[a + 2]) : (a + 1 < N ? fminf(x[a], x[a + 1]) : x[a]);
+    }
+    return tree_min<M>(y);
+  }
+}
+template <int N>
+__device__ __forceinline__ float tree_sum(const float (&x)[N]) {
+  if constexpr (N == 1) {
+    return x[0];
+  } else {
+    constexpr int M = (N + 1) / 2;
+    float y[M];
+#pragma unroll
+    for (int k = 0; k < M; ++k) y[k] = 2 * k + 1 < N ? x[2 * k] + x[2 * k + 1] : x[2 * k];
+    return tree_sum<M>(y);
+  }
+}
+
 // One query row is shared by the lane pair (l, l ^ 32); each lane holds NV scores of it.
 // On entry s[] holds raw dot products q.k; valid(i) tells whether score i's key is allowed
 // (only consulted when kMask). On return s[] holds p (0 for masked keys), lsum includes
@@ -34,16 +79,9 @@ __device__ __forceinline__ float softmax_tile(float (&s)[NV], ValidFn valid,
 #pragma unroll
     for (int i = 0; i < NV; ++i) s[i] = valid(i) ? s[i] : sentinel;
   }
-  float ext = s[0];
-  if (!neg) {
-#pragma unroll
-    for (int i = 1; i < NV; ++i) ext = fmaxf(ext, s[i]);
-    ext = pair32_max(ext);
-  } else {
-#pragma unroll
-    for (int i = 1; i < NV; ++i) ext = fminf(ext, s[i]);
-    ext = pair32_min(ext);
-  }
+  float ext;
+  if (!neg) ext = pair32_max(tree_max(s));
+  else ext = pair32_min(tree_min(s));
   const float mt = (ext == sentinel) ? -kInf : ext * c;
 
   float alpha = 1.0f;
@@ -55,15 +93,19 @@ __device__ __forceinline__ float softmax_tile(float (&s)[NV], ValidFn valid,
     lsum *= alpha;
   }
   const float moff = (m_used == -kInf) ? 0.0f : m_used;
+  // All exponent arguments first, then the exponentials: no exp waits on the product before it.
+  float t[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) t[i] = fmaf(s[i], c, -moff);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    float p = fast_exp2(fmaf(s[i], c, -moff));
+    float p = fast_exp2(t[i]);
     // Allowed scores are finite, so the sentinel marks exactly the masked keys (this also covers
     // c == 0, where the sentinel times c would give NaN).
     if constexpr (kMask) p = (s[i] == sentinel) ? 0.0f : p;
     s[i] = p;
-    lsum += p;
   }
+  lsum += tree_sum(s);
   return alpha;
 }
 

@@ -69,6 +69,26 @@ def test_small_shapes(dtype, d, B, H, Nq, Nk, causal, lens):
     _check(q, k, v, lt, scale, causal, dtype, f"small {dtype} d={d} {B}x{H}x{Nq}x{Nk} causal={causal} lens={lens}")
 
 
+# Nq >= 2048 runs the 8-wave kernel (one wave's matrix work overlapped with its SIMD partner's
+# softmax, 256-row tiles, separate unmasked and masked key loops); these shapes cover its masks,
+# ragged tails, Nq != Nk, padding and empty sequences at both head dimensions.
+LONG = [
+    # B, H, Nq, Nk, d, causal, lens
+    (1, 2, 2048, 2048, 128, True, None),
+    (1, 1, 2113, 2113, 64, True, None),
+    (2, 1, 2048, 2500, 128, False, [2500, 77]),
+    (2, 2, 2300, 1000, 64, False, [1000, 0]),
+    (1, 1, 2304, 2304, 64, False, [1000]),
+    (1, 1, 4096, 4096, 128, True, None),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal,lens", LONG)
+def test_long_sequence_kernel(B, H, Nq, Nk, d, causal, lens):
+    q, k, v, lt, scale = _case(B, H, Nq, Nk, d, "bf16", causal, lens, seed=Nq + Nk + d, std=0.7)
+    _check(q, k, v, lt, scale, causal, "bf16", f"long d={d} {B}x{H}x{Nq}x{Nk} causal={causal} lens={lens}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B,H,Nk,lens", [(1, 1, 1, None), (2, 3, 700, [700, 1]), (3, 2, 513, [0, 256, 257]),
                                           (4, 2, 8192, [8192, 1024, 4097, 5])])
@@ -132,7 +152,7 @@ def test_decode_split_kv_workload():
         compare(og[b0:b0 + 8], lg[b0:b0 + 8], o_ref, lse_ref, "bf16", what=f"{w.name} b{b0}")
 
 
-@pytest.mark.parametrize("Nq", [1, 200])
+@pytest.mark.parametrize("Nq", [1, 200, 2048])
 def test_poisoned_padding_is_bit_identical(Nq):
     B, H, Nk, d = 3, 2, 300, 128
     lens = [300, 45, 129]
@@ -149,9 +169,10 @@ def test_poisoned_padding_is_bit_identical(Nq):
     assert torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("Nq", [1, 1024])
+@pytest.mark.parametrize("Nq", [1, 1024, 2048])
 def test_bitwise_repeatable(Nq):
-    q, k, v, lt, scale = _case(2, 4, Nq, 1024, 128, "bf16", Nq > 1, None, seed=41)
+    Nk = max(Nq, 1024)  # causal (Nq > 1) needs Nq == Nk
+    q, k, v, lt, scale = _case(2, 4, Nq, Nk, 128, "bf16", Nq > 1, None, seed=41)
     o1, l1 = run_lib(q, k, v, scale, Nq > 1, lt)
     o2, l2 = run_lib(q, k, v, scale, Nq > 1, lt)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
@@ -181,15 +202,23 @@ def test_huge_scores_stay_finite(dtype):
     _check(q, k, v, lt, 2.0, True, "bf16", f"huge scores {dtype}")
 
 
+def test_huge_scores_long_sequence_kernel():
+    # The same stress on the 8-wave kernel: large, drifting scores keep moving the running max,
+    # so its lazy rescaling of the output accumulator is exercised many times per row.
+    q, k, _, lt, _ = _case(1, 2, 2048, 2048, 64, "bf16", True, None, seed=62, std=4.0)
+    v = _rand((1, 2, 2048, 64), 65, "bf16")
+    _check(q, k, v, lt, 2.0, True, "bf16", "huge scores, long sequence")
+
+
 @pytest.mark.parametrize("scale", [-0.3, 0.0])
-@pytest.mark.parametrize("Nq", [1, 90])
+@pytest.mark.parametrize("Nq", [1, 90, 2050])
 def test_negative_and_zero_scale(scale, Nq):
     q, k, v, lt, _ = _case(2, 2, Nq, 190, 64, "bf16", False, [190, 60], seed=71)
     _check(q, k, v, lt, scale, False, "bf16", f"scale={scale} Nq={Nq}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("Nq", [1, 40])
+@pytest.mark.parametrize("Nq", [1, 40, 2048])
 def test_empty_sequences_and_no_keys(dtype, Nq):
     if dtype == "fp32" and Nq == 1:
         Nq = 3
