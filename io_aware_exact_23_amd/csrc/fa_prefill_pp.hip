@@ -13,7 +13,7 @@
 // groups of 4, and the groups alternate between two kinds of phase, separated by workgroup
 // barriers:
 //   matrix phase i:  S_i = K_i Q^T (scores of key tile i) and O^T += V_{i-1}^T P_{i-1}^T
-//   softmax phase i: running max / normaliser update, P_i = 2^(t - m) as bf16, O rescale
+//   softmax phase i: P_i = 2^(t - m) as bf16, normaliser update, and (rarely) a new offset m
 // Group 1 runs one phase behind group 0, so in every phase each SIMD has one wave on the matrix
 // cores and one on the vector ALUs. (This is the scheduling idea the pages credit to FA3 for
 // Hopper, page "FlashAttention：把注意力从公式写成数据流", section "FA2 与 FA3", rebuilt with
@@ -30,7 +30,17 @@
 // 2i, 2i+1 of the workgroup timeline. Four LDS slots hold U_i .. U_{i+3}; every wave copies its
 // 1/8 share of each unit from HBM straight into LDS (buffer_load_dwordx4 ... lds, no registers,
 // range-checked so keys past the workgroup's range read as zeros) about three phases before it
-// is needed. V^T operands come from transposing LDS reads (ds_read_b64_tr_b16).
+// is needed. V^T operands come from transposing LDS reads (ds_read_b64_tr_b16). Every LDS
+// operand address is a per-lane register computed once plus an immediate, so a matrix phase
+// issues nothing but LDS reads and MFMAs: a vector instruction in that stream would wait behind
+// the partner wave's softmax work and stall the matrix cores.
+//
+// Lazy offset. The exponent offset m of a row is not the running maximum: it only moves when a
+// tile would make the probabilities too large (this lane's half-row sum of p above 2^12) and on
+// the first tile with an allowed key. With the offset held, p = 2^(t - m) <= 2^12 never
+// overflows, and the usual softmax algebra (O and l both carry the factor 2^-m) is unchanged;
+// the row maximum is computed only on the tiles that move m, so most softmax phases are just
+// one FMA, one exponential and one addition per score plus the bf16 packing.
 #include "fa_device.h"
 #include "fa_params.h"
 #include "fa_softmax.h"
@@ -38,6 +48,26 @@
 #include <type_traits>
 
 namespace fa {
+
+// Maximum of the 32 scores a lane holds for its query row, then across the lane pair (l, l^32)
+// that holds the row's other keys: 16 three-input maxima and one exchange. Written as asm so the
+// compiler adds no NaN-quieting copies of the matrix results in front of each maximum.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float row_max32(const float (&s)[32]) {
+  float a[10];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) a[i] = vmax3(s[3 * i], s[3 * i + 1], s[3 * i + 2]);
+  const float c0 = vmax3(a[0], a[1], a[2]), c1 = vmax3(a[3], a[4], a[5]), c2 = vmax3(a[6], a[7], a[8]);
+  const float c3 = vmax3(a[9], s[30], s[31]);
+  const float x = vmax3(c0, c1, vmax3(c2, c3, c3));
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return vmax3(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
+}
 
 template <int D>
 struct PrefillPPCfg {
@@ -181,6 +211,25 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
     const int sw = 4 * (ta % (C::kNch / 4));
     vt_off[db] = (8 * g + ta) * C::kRowBytes + ((piece ^ sw) << 4) + 8 * (tb & 1);
   }
+  // Per-lane LDS byte offsets of every operand read, computed once. The immediate offset field of
+  // an LDS read holds 16 bits, so for slots 2 and 3 (64 KiB and up when d = 128) each offset has
+  // a copy 64 KiB higher that the immediate subtracts again; the empty asm keeps the compiler
+  // from folding the copies back, so the matrix phase issues no address arithmetic.
+  constexpr int kHi = 4 * C::kUnitBytes > 65536 ? 65536 : 0;
+  uint32_t kofs[2][D / 16], vofs[2][D / 32];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kofs[h][ks] = (uint32_t)(h * kHi + krow_off + (((2 * ks + g) ^ kx) << 4));
+      asm volatile("" : "+v"(kofs[h][ks]));
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      vofs[h][db] = (uint32_t)(h * kHi + vt_off[db]);
+      asm volatile("" : "+v"(vofs[h][db]));
+    }
+  }
 
   f32x16 sacc[2];   // S^T of key tile i (two 32-key blocks), then t = c*s - m in place, then p
 #pragma unroll
@@ -192,63 +241,35 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) pk[kb][hh] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-  bool rescale_pending = false;  // wave-uniform: O must be multiplied by alpha_pending before PV
-  float alpha_pending = 1.0f;
+  constexpr float kSumCap = 4096.0f;  // bound on a lane's half-row sum of p before m moves
 
-  // ---- Matrix phase i: S_i = K_i Q^T, then O^T += V_{i-1}^T P_{i-1}^T, each a software-
-  // pipelined sequence of MFMAs whose LDS operand is read kAhead instructions before the MFMA
-  // that consumes it. While the PV MFMAs run, the same wave does the softmax bookkeeping of
-  // tile i on the vector ALUs (running max, rescale decision, exponent arguments), which this
-  // chip overlaps with the wave's own matrix instructions; only the exponentials, which it does
-  // not overlap, are left for the next phase.
-  // Every iteration runs the same code; the edges are handled by data instead of branches (a
-  // branch would make the compiler copy the accumulators at every join): unit 0 carries V tile
-  // -1 and unit n carries K tile n, both outside the buffer range and read as zeros; P before
-  // tile 0 is zero; and a tile with no allowed key for this wave (tile n, tiles past the wave's
-  // causal diagonal, rows past Nq) is fully masked, so its P is exactly zero.
   constexpr int kAhead = 4;
   constexpr int kNS = 2 * (D / 16);  // S MFMAs: key block kb = m % 2, d step ks = m / 2
   constexpr int kNP = 4 * (D / 32);  // PV MFMAs: d block db = m % (D/32), key step u = m / (D/32)
   constexpr int kNM = kNS + kNP;
 
-  // Running-max update for tile i on the scores in sacc; leaves the base-2 exponent arguments
-  // t = c*s - m in sacc. With kMask, keys this lane may not see (key k0 + 8*g + off with
-  // off = kb*32 + 16*(e/8) + e%8 allowed iff off < rem; rem counts the allowed keys from
-  // k0 + 8*g on: keys < L, keys <= qi when causal, none for rows past Nq) first get -inf, which c
-  // (> 0 here) keeps at t = -inf, so their p is exactly 0. Branch-free, so it shares a basic
-  // block with the matrix instructions.
-  auto update_max = [&](auto mask_tag, int k0) __attribute__((always_inline)) {
+  // Exponent arguments t = c*s - moff of the tile in sacc, written back into sacc. With kMask,
+  // keys this lane may not see (key k0 + 8*g + off with off = kb*32 + 16*(e/8) + e%8 allowed iff
+  // off < rem; rem counts the allowed keys from k0 + 8*g on: keys < L, keys <= qi when causal,
+  // none for rows past Nq) get t = -inf, so their p is exactly 0. Returns whether this lane has
+  // an allowed key in the tile.
+  auto exponent_args = [&](auto mask_tag, int k0, float moff) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
-    float s[32];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb * 16 + e] = sacc[kb][e];
+    int rem = 64;
     if constexpr (kMask) {
       const int qi = qw0 + r32;
-      int rem = (p.causal ? min(L, qi + 1) : L) - (k0 + 8 * g);
+      rem = (p.causal ? min(L, qi + 1) : L) - (k0 + 8 * g);
       if (qi >= p.Nq) rem = 0;
-#pragma unroll
-      for (int x = 0; x < 32; ++x) {
-        const int kb = x >> 4, e = x & 15;
-        s[x] = (kb * 32 + ((e >> 3) << 4) + (e & 7) < rem) ? s[x] : -kInf;
-      }
     }
-    const float ext = pair32_max(tree_max(s));  // the row maximum of t = c*s is max(s)*c
-    const float mt = ext * c;                   // -inf when the whole row is masked
-    // Lazy rescaling: the offset moves only when the tile's maximum passes it by more than kTau.
-    const bool rescaled = wave_any(mt > m_used + kTau);
-    const float mn = rescaled ? fmaxf(m_used, mt) : m_used;
-    const float alpha = (rescaled && m_used != -kInf) ? fast_exp2(m_used - mn) : 1.0f;
-    rescale_pending = rescaled;
-    alpha_pending = alpha;
-    lsum *= alpha;
-    m_used = mn;
-    const float moff = (m_used == -kInf) ? 0.0f : m_used;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kb][e] = fmaf(s[kb * 16 + e], c, -moff);
+      for (int e = 0; e < 16; ++e) {
+        const float t = fmaf(sacc[kb][e], c, -moff);
+        if constexpr (kMask) sacc[kb][e] = (kb * 32 + ((e >> 3) << 4) + (e & 7) < rem) ? t : -kInf;
+        else sacc[kb][e] = t;
+      }
+    return rem > 0;
   };
 
   // ---- Matrix phase i: one software-pipelined sequence of kNM MFMAs, S_i = K_i Q^T and then
@@ -261,17 +282,17 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
   // -1 and unit n carries K tile n, both outside the buffer range and read as zeros; P before
   // tile 0 is zero; and a tile with no allowed key for this wave (tile n, tiles past the wave's
   // causal diagonal, rows past Nq) is fully masked, so its P is exactly zero.
-  auto matrix_phase = [&](const char* unit) __attribute__((always_inline)) {
+  auto matrix_phase = [&](const char* unit, int hs) __attribute__((always_inline)) {
+    const int h = kHi > 0 ? hs : 0;
     const char* Vs = unit + C::kTileBytes;
     auto fetch = [&](int m) -> bf16x8 __attribute__((always_inline)) {
       if (m < kNS) {
         const int kb = m & 1, ks = m >> 1;
-        const char* krow = unit + kb * 32 * C::kRowBytes + krow_off;
-        return *reinterpret_cast<const bf16x8*>(krow + (((2 * ks + g) ^ kx) << 4));
+        return *reinterpret_cast<const bf16x8*>(unit + ((kb * 32 * C::kRowBytes - h * kHi) + (int)kofs[h][ks]));
       }
       const int mp = m - kNS;
       const int db = mp % (D / 32), u = mp / (D / 32);
-      const char* vrow = Vs + u * 16 * C::kRowBytes + vt_off[db];
+      const char* vrow = Vs + ((u * 16 * C::kRowBytes - h * kHi) + (int)vofs[h][db]);
       const s16x4 a8[2] = {lds_read_tr16(vrow), lds_read_tr16(vrow + 4 * C::kRowBytes)};
       return __builtin_bit_cast(bf16x8, a8);
     };
@@ -306,54 +327,87 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
     asm volatile("" : "+v"(pk[0][0]), "+v"(pk[0][1]), "+v"(pk[1][0]), "+v"(pk[1][1]), "+v"(lsum),
                  "+v"(m_used));
   };
-  // ---- Softmax phase for the tile whose scores sit in sacc (key k0 onwards): running max and
-  // rescale decision (update_max), the rescale of O decided there (after the PV of the previous
-  // tile, before the PV of this one), p = 2^t, P -> bf16 B operands, row sums.
+  // ---- Softmax phase for the tile whose scores sit in sacc (key k0 onwards): exponent
+  // arguments, p = 2^t, the row sums, the lazy offset update with its rescale of O (after the PV
+  // of the previous tile, before the PV of this one), P -> bf16 B operands. Runs at raised wave
+  // priority: on a SIMD whose other wave issues matrix instructions, the exponentials otherwise
+  // lose most issue cycles to it, and the softmax is the longer of the two phases.
   auto softmax_phase = [&](auto mask_tag, int k0) __attribute__((always_inline)) {
-    update_max(mask_tag, k0);
-    if (rescale_pending) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha_pending;
-    }
+    const float moff = (m_used == -kInf) ? 0.0f : m_used;
+    const bool any_key = exponent_args(mask_tag, k0, moff);
     float pr[32];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) pr[kb * 16 + e] = fast_exp2(sacc[kb][e]);
+    float ps = tree_sum(pr);
+    // Lazy offset: keep m while this lane's half-row sum of p stays <= kSumCap (then every
+    // p <= kSumCap, so nothing overflows); otherwise, and on the row's first tile with an allowed
+    // key, move m to the row maximum, redo the exponentials against it and rescale O and l by
+    // 2^(m_old - m_new). The decision is wave-wide, so both lanes of a row take the same path.
+    if (wave_any(ps > kSumCap || (m_used == -kInf && any_key))) {
+      float t[32];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) t[kb * 16 + e] = sacc[kb][e];
+      const float mt = row_max32(t) + moff;  // row maximum of c*s; -inf when the row is masked
+      const float mn = fmaxf(m_used, mt);
+      const float alpha = (m_used == -kInf) ? 1.0f : fast_exp2(m_used - mn);
+      const float shift = ((mn == -kInf) ? 0.0f : mn) - moff;
+#pragma unroll
+      for (int x = 0; x < 32; ++x) pr[x] = fast_exp2(t[x] - shift);
+      ps = tree_sum(pr);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      lsum *= alpha;
+      m_used = mn;
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         u32x4 x;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          x[t] = pack_bf16(pr[kb * 16 + hh * 8 + 2 * t], pr[kb * 16 + hh * 8 + 2 * t + 1]);
+        for (int q = 0; q < 4; ++q)
+          x[q] = pack_bf16(pr[kb * 16 + hh * 8 + 2 * q], pr[kb * 16 + hh * 8 + 2 * q + 1]);
         pk[kb][hh] = __builtin_bit_cast(bf16x8, x);
       }
-    lsum += tree_sum(pr);
+    lsum += ps;
     pin_softmax();
   };
 
   // One barrier interval i per key tile. Every wave issues its share of U_{i+3} into `ahead`, the
   // slot that held U_{i-1} (consumed by both groups before the last barrier), outside its matrix
   // phase. Group 0 runs matrix phase i (S_i, PV_{i-1}) and then the softmax of tile i; group 1
-  // runs the softmax of tile i-1 and then matrix phase i. So while a wave of one group works on the vector ALUs the
-  // wave of the other group on its SIMD issues matrix instructions. Before the barrier, this
-  // wave's share of U_{i+1} must have landed; U_{i+2} and U_{i+3} may still be in flight (loads
-  // get three intervals). kMask selects the masked softmax (group 1 applies it to tile i-1).
-  auto interval = [&](auto order_tag, auto mask_tag, int i, const char* unit, char* ahead)
+  // runs the softmax of tile i-1 and then matrix phase i. So while a wave of one group works on
+  // the vector ALUs, the wave of the other group on its SIMD issues matrix instructions; the
+  // softmax runs at wave priority 1, the matrix phase at 0. Before the barrier, this wave's share
+  // of U_{i+1} must have landed; U_{i+2} and U_{i+3} may still be in flight (loads get three
+  // intervals). hs selects the slot's LDS offset copy; kMask selects the masked softmax (group 1
+  // applies it to tile i-1).
+  auto set_prio = [&](int pr) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (pr) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto interval = [&](auto order_tag, auto mask_tag, int i, const char* unit, int hs, char* ahead)
       __attribute__((always_inline)) {
     constexpr bool kMatrixFirst = decltype(order_tag)::value;
     if constexpr (kMatrixFirst) {
-      matrix_phase(unit);
+      matrix_phase(unit, hs);
       issue_unit(i + 3, ahead);
+      set_prio(1);
       softmax_phase(mask_tag, i * C::kBN);
+      set_prio(0);
     } else {
       issue_unit(i + 3, ahead);
+      set_prio(1);
       softmax_phase(mask_tag, (i - 1) * C::kBN);
-      matrix_phase(unit);
+      set_prio(0);
+      matrix_phase(unit, hs);
     }
     wait_vmcnt<2 * C::kLoadsPerUnit>();
     wg_barrier();
@@ -372,18 +426,18 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
   auto run = [&](auto order_tag) __attribute__((always_inline)) {
     int i = 0;
     for (; i < i_mask; i += 4) {
-      interval(order_tag, std::false_type{}, i, slot0, slot3);
-      interval(order_tag, std::false_type{}, i + 1, slot1, slot0);
-      interval(order_tag, std::false_type{}, i + 2, slot2, slot1);
-      interval(order_tag, std::false_type{}, i + 3, slot3, slot2);
+      interval(order_tag, std::false_type{}, i, slot0, 0, slot3);
+      interval(order_tag, std::false_type{}, i + 1, slot1, 0, slot0);
+      interval(order_tag, std::false_type{}, i + 2, slot2, 1, slot1);
+      interval(order_tag, std::false_type{}, i + 3, slot3, 1, slot2);
     }
     for (; i <= n; i += 4) {
-      interval(order_tag, std::true_type{}, i, slot0, slot3);
+      interval(order_tag, std::true_type{}, i, slot0, 0, slot3);
       if (i + 1 <= n) {
-        interval(order_tag, std::true_type{}, i + 1, slot1, slot0);
+        interval(order_tag, std::true_type{}, i + 1, slot1, 0, slot0);
         if (i + 2 <= n) {
-          interval(order_tag, std::true_type{}, i + 2, slot2, slot1);
-          if (i + 3 <= n) interval(order_tag, std::true_type{}, i + 3, slot3, slot2);
+          interval(order_tag, std::true_type{}, i + 2, slot2, 1, slot1);
+          if (i + 3 <= n) interval(order_tag, std::true_type{}, i + 3, slot3, 1, slot2);
         }
       }
     }
