@@ -7,7 +7,11 @@ decode workload (B=64, H=32, Nk=8192 cache with valid lengths in [1024, 8192], d
 the same run and reported under "decode". Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode]
-                  [--no-cpu-baseline] [--cpu-seconds S] [--calibrate-copy]
+                  [--no-standard] [--no-cpu-baseline] [--cpu-seconds S] [--calibrate-copy]
+
+The standard (materialising) algorithm, fa_std_fwd, is timed on the three prefill workloads and
+reported under "standard_attention" with its speedup ratio against fa_fwd (the pages' headline
+comparison) and the HBM roofline of the whole call on the default workload.
 
 FLOPs are counted as 4*B*H*Nq*Nk*d, halved for causal masking. Decode bytes are the algorithmic
 HBM bytes: Q, the valid K and V rows, O and lse.
@@ -32,6 +36,8 @@ PEAK_MFMA_BF16_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 2.4 GHz x 4096 FL
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 KERNEL_SOURCES = ["fa_prefill_bf16.hip", "fa_prefill_pp.hip", "fa_decode.hip", "fa_device.h", "fa_softmax.h",
                   "fa_params.h", "fa_api.cpp"]
+PREFILL_WORKLOADS = ["gpt2s_causal_b8_h12_n1024_d64", "bertl_padded_b16_h16_n512_d64",
+                     "long_causal_b2_h16_n16384_d128"]
 LONG_NQ = 2048  # fa_fwd runs prefill_bf16_pp_kernel from this many query rows on
 
 
@@ -128,6 +134,65 @@ def cpu_baseline_prefill(w, q, k, v, seconds: float):
                       f"as 4*d per (query row, allowed key)"}
 
 
+def allowed_scores(w, lens) -> int:
+    """Number of (query, key) pairs the mask allows, over all (b, h)."""
+    L = np.full(w.B, w.Nk, dtype=np.int64) if lens is None else np.clip(np.asarray(lens, dtype=np.int64), 0, w.Nk)
+    i = np.arange(w.Nq, dtype=np.int64)
+    per_b = np.array([np.minimum(Lb, i + 1).sum() if w.causal else w.Nq * Lb for Lb in L], dtype=np.int64)
+    return int(per_b.sum()) * w.H
+
+
+def standard_bytes(w, lens) -> int:
+    """Algorithmic HBM bytes of the standard algorithm as fa_std_fwd runs it: write S (fp32, full
+    Nq x Nk grid), read the allowed part of S, write P (bf16, rows of ld entries), read P, plus
+    Q, the valid K and V rows, O and lse."""
+    ld = (w.Nk + 127) // 128 * 128
+    bh = w.B * w.H
+    L = np.full(w.B, w.Nk) if lens is None else np.clip(np.asarray(lens), 0, w.Nk)
+    qo = 2 * bh * w.Nq * w.d * 2 + bh * w.Nq * 4
+    kv = 2 * int(L.sum()) * w.H * w.d * 2
+    return int(qo + kv + bh * w.Nq * w.Nk * 4 + allowed_scores(w, lens) * 4 + 2 * bh * w.Nq * ld * 2)
+
+
+def bench_standard(fa, configs, inputs, torch, dev, steps, warmup, main_name):
+    """Standard algorithm against the tiled path on the prefill workloads."""
+    out = {"unit": "ms", "workloads": []}
+    for name in PREFILL_WORKLOADS:
+        w = configs.BY_NAME[name]
+        q, k, v, lens = inputs.make(w, dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+        need = fa.fa_std_workspace_bytes(w.B, w.H, w.Nq, w.Nk)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+        def tiled():
+            fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal), lens, None)
+
+        def standard():
+            fa.fa_std_fwd(q, k, v, o, lse, w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal), lens,
+                          ws, need, None)
+
+        n = steps if w.Nq <= LONG_NQ else max(3, steps // 4)
+        t_tiled, _ = time_launches(tiled, n, warmup, torch)
+        t_std, per_std = time_launches(standard, n, warmup, torch)
+        lens_np = None if lens is None else lens.cpu().numpy()
+        nbytes = standard_bytes(w, lens_np)
+        avg = float(np.mean(per_std))
+        rec = {"workload": name, "tiled_ms": round(t_tiled / n * 1e3, 4), "standard_ms": round(t_std / n * 1e3, 4),
+               "speedup": round(t_std / t_tiled, 2), "workspace_bytes": need,
+               "standard_algorithmic_bytes": nbytes,
+               "standard_hbm_GBps": round(nbytes / avg / 1e9, 1)}
+        if name == main_name:
+            rec["roofline"] = {"kernel": "std_scores_kernel + std_softmax_kernel + std_pv_kernel (whole call)",
+                               "bound": "hbm", "achieved": round(nbytes / avg / 1e9, 1), "peak": PEAK_HBM_GBS,
+                               "unit": "GB/s", "frac": round(nbytes / avg / 1e9 / PEAK_HBM_GBS, 4),
+                               "avg_launch_ms": round(avg * 1e3, 4)}
+        out["workloads"].append(rec)
+        del ws, q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return out
+
+
 def decode_bytes(w, lens) -> int:
     per_key = 2 * w.d * 2                      # one K row and one V row, bf16
     per_bh = 2 * w.d * 2 + 4                   # Q and O rows (bf16) and lse (fp32)
@@ -141,6 +206,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_causal_b2_h16_n16384_d128")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-standard", action="store_true",
+                    help="skip the standard-algorithm comparison (fa_std_fwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -232,6 +299,10 @@ def main():
                          "traffic": traffic_from_profile("decode_split_kernel", wd.name, sha)},
         }
         del dq, dk, dv, do
+
+    if not args.no_standard and w.Nq > 1 and w.dtype == "bf16":
+        result["standard_attention"] = bench_standard(fa, configs, inputs, torch, dev, args.steps,
+                                                      args.warmup, w.name)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)  # 1 GiB

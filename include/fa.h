@@ -32,6 +32,7 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -65,6 +66,29 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int H, int Nq, int Nk, int d, float scale, int causal,
                const int32_t* kv_seqlens, void* stream);
+
+/*
+ * fa_std_fwd -- the same bf16 operation computed by the standard, materialising algorithm, the
+ * baseline the tiled path is measured against (page "FlashAttention：把注意力从公式写成数据流",
+ * opening paragraph: S = Q K^T is written to device memory, read back for the softmax, and P is
+ * written and read again for P V). Three kernels: S = scale * Q K^T over the full Nq x Nk grid in
+ * fp32; a row softmax that applies the mask, writes P as bf16 (0 where masked) and lse; O = P V
+ * over all Nk keys with fp32 accumulation, O rounded to bf16 once.
+ *   Same arguments and rules as fa_fwd (any Nq, including 1, runs these kernels), plus:
+ *   workspace        device memory owned by the caller, 256-byte aligned, at least
+ *                    fa_std_workspace_bytes(B, H, Nq, Nk) bytes (may be NULL when that is 0).
+ *                    It receives S ([B][H][Nq][ld] fp32) followed by P ([B][H][Nq][ld] bf16),
+ *                    ld = Nk rounded up to a multiple of 128; on return it holds S and P.
+ *   workspace_bytes  its size; smaller than required -> FA_ERR_INVALID_ARGUMENT.
+ *   One head's S must stay below 2^31 bytes (Nq * ld * 4), else FA_ERR_UNSUPPORTED.
+ * As with fa_fwd, key rows at or past L_b are never read.
+ */
+int fa_std_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Nq, int Nk, int d, float scale, int causal,
+               const int32_t* kv_seqlens, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fa_std_fwd needs: 6 * B * H * Nq * ld (0 if any size is <= 0). */
+size_t fa_std_workspace_bytes(int B, int H, int Nq, int Nk);
 
 /* Static description of a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -9,11 +9,16 @@ Entry points mirror the C ABI in ``include/fa.h``:
 
 * ``fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, stream)`` -- bf16
 * ``fa_fwd_f32(...)``                                                          -- fp32
+* ``fa_std_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, workspace,
+  workspace_bytes, stream)`` -- bf16, standard (materialising) algorithm, the baseline
+* ``fa_std_workspace_bytes(B, H, Nq, Nk)``
 * ``fa_status_string(status)``, ``fa_last_error()``
 
 Pointer arguments accept a torch tensor (its ``data_ptr()``), an int address or None; ``stream``
 accepts a ``torch.cuda.Stream``, an int handle or None (the current torch stream).
-``attention(q, k, v, ...)`` allocates O and lse with torch and calls the right entry point.
+``attention(q, k, v, ...)`` allocates O and lse with torch and calls the right entry point;
+``standard_attention(q, k, v, ...)`` does the same for ``fa_std_fwd`` (bf16 only), allocating
+its workspace with torch unless one is passed.
 """
 
 from __future__ import annotations
@@ -23,8 +28,9 @@ import math
 import os
 from typing import Optional, Tuple
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_status_string", "fa_last_error", "attention",
-           "library_path", "load_library"]
+__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_std_fwd", "fa_std_workspace_bytes",
+           "fa_status_string", "fa_last_error", "attention", "standard_attention", "library_path",
+           "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfa.so")
@@ -62,6 +68,10 @@ def load_library():
         fn = getattr(lib, name)
         fn.argtypes = sig
         fn.restype = ci
+    lib.fa_std_fwd.argtypes = sig[:13] + [vp, ctypes.c_size_t, vp]
+    lib.fa_std_fwd.restype = ci
+    lib.fa_std_workspace_bytes.argtypes = [ci, ci, ci, ci]
+    lib.fa_std_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [ci]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -114,9 +124,23 @@ def fa_fwd_f32(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens=None,
     _call("fa_fwd_f32", q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, stream)
 
 
-def attention(q, k, v, scale: Optional[float] = None, causal: bool = False, kv_seqlens=None,
-              out=None, lse=None, stream=None) -> Tuple["object", "object"]:
-    """O, lse for device tensors q [B,H,Nq,d] and k, v [B,H,Nk,d] (bf16 or fp32, contiguous)."""
+def fa_std_workspace_bytes(B, H, Nq, Nk) -> int:
+    """Workspace bytes fa_std_fwd needs; see include/fa.h."""
+    return int(load_library().fa_std_workspace_bytes(int(B), int(H), int(Nq), int(Nk)))
+
+
+def fa_std_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, workspace,
+               workspace_bytes, stream=None) -> None:
+    """bf16 forward by the standard algorithm; see include/fa.h for the contract."""
+    lib = load_library()
+    st = lib.fa_std_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq),
+                        int(Nk), int(d), float(scale), int(causal), _ptr(kv_seqlens),
+                        _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, f"{fa_status_string(st)} ({fa_last_error()})")
+
+
+def _check_qkv(q, k, v, kv_seqlens, dtypes):
     import torch
 
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -125,14 +149,45 @@ def attention(q, k, v, scale: Optional[float] = None, causal: bool = False, kv_s
     Nk = k.shape[2]
     if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
         raise ValueError("k and v must be [B, H, Nk, d] matching q")
-    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in dtypes:
+        raise ValueError("q, k, v must share one of the dtypes " + ", ".join(map(str, dtypes)))
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors")
     if kv_seqlens is not None:
         if kv_seqlens.dtype != torch.int32 or not kv_seqlens.is_cuda or kv_seqlens.numel() != B:
             raise ValueError("kv_seqlens must be an int32 device tensor of length B")
+    return B, H, Nq, Nk, d
+
+
+def standard_attention(q, k, v, scale: Optional[float] = None, causal: bool = False,
+                       kv_seqlens=None, out=None, lse=None, workspace=None,
+                       stream=None) -> Tuple["object", "object"]:
+    """O, lse by the standard algorithm (S and P through device memory), bf16 inputs."""
+    import torch
+
+    B, H, Nq, Nk, d = _check_qkv(q, k, v, kv_seqlens, (torch.bfloat16,))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    need = fa_std_workspace_bytes(B, H, Nq, Nk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    fa_std_fwd(q, k, v, out, lse, B, H, Nq, Nk, d, scale, int(bool(causal)), kv_seqlens,
+               workspace, wbytes, stream)
+    return out, lse
+
+
+def attention(q, k, v, scale: Optional[float] = None, causal: bool = False, kv_seqlens=None,
+              out=None, lse=None, stream=None) -> Tuple["object", "object"]:
+    """O, lse for device tensors q [B,H,Nq,d] and k, v [B,H,Nk,d] (bf16 or fp32, contiguous)."""
+    import torch
+
+    B, H, Nq, Nk, d = _check_qkv(q, k, v, kv_seqlens, (torch.bfloat16, torch.float32))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:

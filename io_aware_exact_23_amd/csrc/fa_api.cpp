@@ -14,6 +14,7 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream
 hipError_t launch_prefill_bf16_pp(const PrefillParams& p, int d, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);
+hipError_t launch_standard(const StandardParams& p, int d, hipStream_t stream);
 int prefill_bf16_rows_per_wg(int d);
 constexpr int kPrefillLongNq = 2048;  // query rows from which the 8-wave prefill kernel is used
 int decode_chunk();
@@ -148,6 +149,62 @@ extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float*
   fa::PrefillParams p = prefill_params(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_seqlens);
   hipError_t e = fa::launch_prefill_f32(p, d, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail_hip(e, "prefill launch");
+  return FA_OK;
+}
+
+namespace {
+// Row stride (elements) of the standard path's S and P buffers: Nk rounded up to a whole 128-key
+// tile, so that every tile the kernels touch lies inside its row.
+int64_t std_ld(int Nk) { return ((int64_t)Nk + 127) / 128 * 128; }
+}  // namespace
+
+extern "C" size_t fa_std_workspace_bytes(int B, int H, int Nq, int Nk) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0) return 0;
+  const double bytes = (double)B * H * Nq * (double)std_ld(Nk) * 6.0;
+  if (bytes > 9.0e18) return 0;
+  return (size_t)B * H * (size_t)Nq * (size_t)std_ld(Nk) * 6u;
+}
+
+extern "C" int fa_std_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                          const int32_t* kv_seqlens, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  const int64_t ld = std_ld(Nk);
+  if ((int64_t)Nq * ld * 4 > std::numeric_limits<int32_t>::max())
+    return fail(FA_ERR_UNSUPPORTED, "Nq * Nk too large for one head's score matrix");
+  const int64_t bh = (int64_t)B * H;
+  if (bh * Nq > std::numeric_limits<int32_t>::max() ||
+      bh * ((Nq + 127) / 128) * ((Nk + 127) / 128) > std::numeric_limits<int32_t>::max())
+    return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  const size_t need = fa_std_workspace_bytes(B, H, Nq, Nk);
+  if (need > 0) {
+    if (!workspace) return fail(FA_ERR_INVALID_ARGUMENT, "workspace must be non-null");
+    if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_INVALID_ARGUMENT, "workspace smaller than fa_std_workspace_bytes()");
+  }
+  fa::StandardParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.kv_seqlens = kv_seqlens;
+  p.s = static_cast<float*>(workspace);
+  p.pm = need > 0 ? reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + (size_t)bh * Nq * ld * 4)
+                  : nullptr;
+  p.B = B;
+  p.H = H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.ld = (int)ld;
+  p.scale = scale;
+  p.causal = causal;
+  hipError_t e = fa::launch_standard(p, d, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "standard attention launch");
   return FA_OK;
 }
 

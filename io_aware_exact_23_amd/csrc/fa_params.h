@@ -35,4 +35,20 @@ struct DecodeParams {
   float c;            // scale * log2(e)
 };
 
+// Standard (materialising) attention: S = scale * Q K^T and P = softmax(S) both go to device
+// memory, then O = P V. Rows of S and P are ld elements apart (ld = Nk rounded up to 64).
+struct StandardParams {
+  const void* q;  // [B][H][Nq][D] bf16
+  const void* k;  // [B][H][Nk][D] bf16
+  const void* v;  // [B][H][Nk][D] bf16
+  void* o;        // [B][H][Nq][D] bf16
+  float* lse;     // [B][H][Nq]
+  const int32_t* kv_seqlens;  // [B] or nullptr
+  float* s;       // [B][H][Nq][ld] fp32 scores
+  uint16_t* pm;   // [B][H][Nq][ld] bf16 probabilities
+  int B, H, Nq, Nk, ld;
+  float scale;
+  int causal;
+};
+
 }  // namespace fa

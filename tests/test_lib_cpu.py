@@ -23,7 +23,8 @@ def declared_functions():
 
 
 def test_header_declares_the_abi():
-    assert declared_functions() == ["fa_fwd", "fa_fwd_f32", "fa_last_error", "fa_status_string"]
+    assert declared_functions() == ["fa_fwd", "fa_fwd_f32", "fa_last_error", "fa_status_string",
+                                    "fa_std_fwd", "fa_std_workspace_bytes"]
 
 
 @needs_lib
@@ -45,8 +46,19 @@ A = 0x10000000
 BAD = 0x10000001
 
 
+def _std(**kw):
+    """fa_std_fwd with the fa_fwd keyword set plus a (fake) large enough workspace."""
+    ws = kw.pop("workspace", A)
+    wb = kw.pop("workspace_bytes", 1 << 40)
+    fa.fa_std_fwd(workspace=ws, workspace_bytes=wb, **kw)
+
+
+ENTRY = {"fa_fwd": lambda **kw: fa.fa_fwd(**kw), "fa_fwd_f32": lambda **kw: fa.fa_fwd_f32(**kw),
+         "fa_std_fwd": _std}
+
+
 @needs_lib
-@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32", "fa_std_fwd"])
 @pytest.mark.parametrize("args,status,needle", [
     (dict(d=96), fa.FA_ERR_UNSUPPORTED, "64 or 128"),
     (dict(d=0), fa.FA_ERR_UNSUPPORTED, "64 or 128"),
@@ -70,19 +82,53 @@ def test_argument_errors(fn, args, status, needle):
                 kv_seqlens=None, stream=0)
     call.update(args)
     with pytest.raises(fa.FaError) as ei:
-        getattr(fa, fn)(**call)
+        ENTRY[fn](**call)
     assert ei.value.status == status
     assert needle in ei.value.message
 
 
 @needs_lib
-@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+@pytest.mark.parametrize("args,needle", [
+    (dict(workspace=None), "non-null"),
+    (dict(workspace=A + 128), "256-byte aligned"),
+    (dict(workspace_bytes=2 * 3 * 8 * 128 * 6 - 1), "smaller"),
+])
+def test_standard_workspace_errors(args, needle):
+    # B=2, H=3, Nq=8, Nk=8: S and P rows are padded to 128 keys, 6 bytes per entry.
+    call = dict(q=A, k=A, v=A, o=A, lse=A, B=2, H=3, Nq=8, Nk=8, d=64, scale=0.125, causal=0,
+                kv_seqlens=None, stream=0)
+    call.update(args)
+    with pytest.raises(fa.FaError) as ei:
+        _std(**call)
+    assert ei.value.status == fa.FA_ERR_INVALID_ARGUMENT
+    assert needle in ei.value.message
+
+
+@needs_lib
+def test_standard_workspace_size():
+    assert fa.fa_std_workspace_bytes(2, 3, 8, 8) == 2 * 3 * 8 * 128 * 6
+    assert fa.fa_std_workspace_bytes(1, 1, 1, 129) == 256 * 6
+    assert fa.fa_std_workspace_bytes(2, 16, 16384, 16384) == 2 * 16 * 16384 * 16384 * 6
+    for args in [(0, 1, 1, 1), (1, 0, 1, 1), (1, 1, 0, 1), (1, 1, 1, 0), (-1, 1, 1, 1)]:
+        assert fa.fa_std_workspace_bytes(*args) == 0
+
+
+@needs_lib
+def test_standard_rejects_a_head_too_large():
+    with pytest.raises(fa.FaError) as ei:
+        _std(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, Nq=32768, Nk=32768, d=64, scale=0.1, causal=0,
+             kv_seqlens=None, stream=0)
+    assert ei.value.status == fa.FA_ERR_UNSUPPORTED
+
+
+@needs_lib
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32", "fa_std_fwd"])
 @pytest.mark.parametrize("args", [dict(B=0), dict(H=0), dict(Nq=0), dict(B=0, q=None, o=None, lse=None)])
 def test_empty_batch_is_a_no_op(fn, args):
     call = dict(q=A, k=A, v=A, o=A, lse=A, B=2, H=3, Nq=8, Nk=8, d=128, scale=0.1, causal=0,
                 kv_seqlens=None, stream=0)
     call.update(args)
-    getattr(fa, fn)(**call)  # returns FA_OK without launching anything
+    ENTRY[fn](**call)  # returns FA_OK without launching anything
     assert fa.fa_last_error() == ""
 
 
