@@ -19,9 +19,13 @@ probability matrix P materialised for one (batch, head) at a time.
 
 For batch b, head h and query row i:
 
-* allowed keys   A_i = { j : j < L_b  and  (not causal  or  j <= i) }
+* allowed keys   A_i = { j : j < L_b  and  (not causal  or  j <= i)
+                         and (left < 0 or j >= i - left)  and  (right < 0 or j <= i + right) }
                  (L_b = kv_seqlens[b] clamped to [0, Nk], or Nk when no lengths are given;
-                 invalid positions must not enter the normalisation: [dataflow] section
+                 (left, right) is an optional sliding window around key position i, -1 on a
+                 side meaning no limit there; invalid positions must not enter the
+                 normalisation, and sliding windows are one of the mask kinds named next to
+                 causal masks and variable-length batches: [dataflow] section
                  "精度、掩码和边界情况")
 * scores         S_ij = scale * sum_k q_ik k_jk            for j in A_i
 * softmax        m_i = max_{j in A_i} S_ij,  e_ij = exp(S_ij - m_i),  l_i = sum_j e_ij,
@@ -32,7 +36,8 @@ For batch b, head h and query row i:
 
 Readings taken where the pages are silent: the scale is an argument (the workloads use
 1/sqrt(d)); lse is the natural-log logsumexp of the scaled, masked scores; causal masking is
-defined only for Nq == Nk; padded query rows are computed like any other row. The max shift
+defined only for Nq == Nk; padded query rows are computed like any other row; a window places
+query i at key position i (the same alignment as the causal mask), for any Nq and Nk. The max shift
 m_i changes nothing in exact arithmetic; it keeps exp finite for large scores.
 
 Every quantity is fp64. Inputs arrive as fp64 arrays that hold bf16 or fp32 values exactly
@@ -62,17 +67,24 @@ def _length(kv_seqlens, b: int, nk: int) -> int:
     return int(min(max(int(kv_seqlens[b]), 0), nk))
 
 
-def allowed_mask(rows: np.ndarray, nk: int, length: int, causal: bool) -> np.ndarray:
+def allowed_mask(rows: np.ndarray, nk: int, length: int, causal: bool, window=None) -> np.ndarray:
     """Boolean matrix M[r, j] = (key j is in A_{rows[r]})."""
     j = np.arange(nk)[None, :]
+    i = np.asarray(rows)[:, None]
     ok = j < length
     if causal:
-        ok = ok & (j <= np.asarray(rows)[:, None])
+        ok = ok & (j <= i)
+    if window is not None:
+        left, right = int(window[0]), int(window[1])
+        if left >= 0:
+            ok = ok & (j >= i - left)
+        if right >= 0:
+            ok = ok & (j <= i + right)
     return np.broadcast_to(ok, (len(rows), nk)).copy()
 
 
 def attention_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.ndarray,
-                   scale: float, causal: bool, length: int, return_p: bool = False):
+                   scale: float, causal: bool, length: int, return_p: bool = False, window=None):
     """The definition for one (batch, head) and a set of query rows.
 
     q_rows: (R, d) fp64, the query vectors of the rows listed in ``rows`` (their indices i).
@@ -83,7 +95,7 @@ def attention_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.nd
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     nk = k.shape[0]
-    ok = allowed_mask(rows, nk, length, causal)
+    ok = allowed_mask(rows, nk, length, causal, window)
 
     # S = scale * Q K^T, with masked entries at -inf (they never enter the normalisation).
     s = np.full((len(rows), nk), -np.inf)
@@ -108,13 +120,15 @@ def attention_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.nd
 
 
 def attention_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                  causal: bool = False, kv_seqlens=None, rows=None, return_p: bool = False):
+                  causal: bool = False, kv_seqlens=None, rows=None, return_p: bool = False,
+                  window=None):
     """Exact attention for a whole batch.
 
     q: (B, H, Nq, d); k, v: (B, H, Nk, d); all fp64 (or anything numpy turns into fp64 exactly).
     kv_seqlens: None or a length-B integer sequence (valid key count per sequence).
     rows: None for every query row, else a 1-D array of query indices evaluated for every
           (b, h) -- each row of the definition depends only on its own query vector.
+    window: None, or (left, right) with -1 for an unlimited side (see A_i above).
     Returns O (B, H, R, d) and lse (B, H, R) with R = Nq or len(rows); also P (B, H, R, Nk)
     when ``return_p``.
     """
@@ -133,7 +147,7 @@ def attention_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
         length = _length(kv_seqlens, b, nk)
         for h in range(heads):
             res = attention_rows(q[b, h, idx], k[b, h], v[b, h], idx, scale, causal, length,
-                                 return_p=return_p)
+                                 return_p=return_p, window=window)
             o[b, h], lse[b, h] = res[0], res[1]
             if return_p:
                 p_all[b, h] = res[2]

@@ -223,3 +223,109 @@ def pin_large_scores(impl):
 ALL_PINS = [pin_brute_force, pin_golden, pin_zero_query_is_mean, pin_single_key, pin_constant_v,
             pin_causal_first_row, pin_probabilities, pin_key_permutation, pin_key_shift,
             pin_large_scores]
+
+
+# ---- sliding windows: impl(q, k, v, scale, causal=False, kv_seqlens=None, return_p=False,
+# window=None), window = (left, right) with -1 for an unlimited side; query i sits at key i.
+
+def brute_force_window_mp(q, k, v, scale, lens, window, digits=50):
+    """The windowed definition at ``digits`` digits, no max shift, from the allowed set written
+    out key by key."""
+    left, right = window
+    mpmath.mp.dps = digits
+    bsz, heads, nq, d = q.shape
+    nk = k.shape[2]
+    o = np.zeros((bsz, heads, nq, v.shape[3]))
+    lse = np.zeros((bsz, heads, nq))
+    for b in range(bsz):
+        length = nk if lens is None else min(max(int(lens[b]), 0), nk)
+        for h in range(heads):
+            for i in range(nq):
+                allowed = [j for j in range(nk)
+                           if j < length and (left < 0 or i - j <= left) and (right < 0 or j - i <= right)]
+                if not allowed:
+                    o[b, h, i] = 0.0
+                    lse[b, h, i] = -np.inf
+                    continue
+                ex = {}
+                for j in allowed:
+                    acc = mpmath.fsum(mpmath.mpf(float(q[b, h, i, t])) * mpmath.mpf(float(k[b, h, j, t]))
+                                      for t in range(d))
+                    ex[j] = mpmath.exp(mpmath.mpf(float(scale)) * acc)
+                z = mpmath.fsum(ex.values())
+                for t in range(v.shape[3]):
+                    o[b, h, i, t] = float(mpmath.fsum(ex[j] * mpmath.mpf(float(v[b, h, j, t])) for j in allowed) / z)
+                lse[b, h, i] = float(mpmath.log(z))
+    return o, lse
+
+
+def pin_window_brute_force(impl):
+    cases = [
+        # (B, H, Nq, Nk, d, lens, window, seed)
+        (1, 1, 7, 7, 2, None, (2, 0), 21),
+        (2, 1, 6, 6, 3, [6, 4], (1, 1), 22),
+        (1, 2, 5, 9, 2, None, (0, 3), 23),
+        (2, 1, 8, 8, 2, [8, 3], (3, -1), 24),
+        (1, 1, 9, 5, 3, None, (-1, 2), 25),
+    ]
+    for bsz, heads, nq, nk, d, lens, window, seed in cases:
+        r = _rng(seed)
+        q = r.standard_normal((bsz, heads, nq, d))
+        k = r.standard_normal((bsz, heads, nk, d))
+        v = r.standard_normal((bsz, heads, nk, d + 1))
+        o, lse = impl(q, k, v, 0.9, False, lens, window=window)
+        o_ref, lse_ref = brute_force_window_mp(q, k, v, 0.9, lens, window)
+        _close(o, o_ref, 1e-12, f"O window brute force seed={seed}")
+        _close(lse, lse_ref, 1e-12, f"lse window brute force seed={seed}")
+
+
+def pin_window_diagonal(impl):
+    # Window (0, 0): each query sees only key i, so O_i = V_i and lse_i = scale * q_i . k_i
+    # (rows i >= min(Nk, L_b) see nothing).
+    r = _rng(26)
+    q = r.standard_normal((2, 2, 6, 4))
+    k = r.standard_normal((2, 2, 6, 4))
+    v = r.standard_normal((2, 2, 6, 4))
+    o, lse = impl(q, k, v, 0.4, False, [6, 4], window=(0, 0))
+    diag = 0.4 * np.sum(q * k, axis=-1)
+    for b, length in enumerate((6, 4)):
+        _close(o[b, :, :length], v[b, :, :length], 1e-15, "window (0,0) O_i = V_i")
+        _close(lse[b, :, :length], diag[b, :, :length], 1e-14, "window (0,0) lse_i = S_ii")
+        assert np.all(o[b, :, length:] == 0.0) and np.all(np.isneginf(lse[b, :, length:]))
+
+
+def pin_window_reductions(impl):
+    # (-1, 0) is the causal mask; (-1, -1) and any window wider than the sequence are no mask.
+    r = _rng(27)
+    q = r.standard_normal((2, 2, 7, 3))
+    k = r.standard_normal((2, 2, 7, 3))
+    v = r.standard_normal((2, 2, 7, 3))
+    for lens in (None, [7, 2]):
+        oc, lc = impl(q, k, v, 0.6, True, lens)
+        ow, lw = impl(q, k, v, 0.6, False, lens, window=(-1, 0))
+        _close(ow, oc, 1e-15, "window (-1,0) = causal O")
+        _close(lw, lc, 1e-15, "window (-1,0) = causal lse")
+        on, ln_ = impl(q, k, v, 0.6, False, lens)
+        for wnd in ((-1, -1), (6, 6), (100, -1)):
+            ow, lw = impl(q, k, v, 0.6, False, lens, window=wnd)
+            _close(ow, on, 1e-15, f"window {wnd} = no mask O")
+            _close(lw, ln_, 1e-15, f"window {wnd} = no mask lse")
+
+
+def pin_window_probabilities(impl):
+    # Keys outside the window get exactly zero weight; inside, positive weights summing to 1.
+    r = _rng(28)
+    q = r.standard_normal((1, 2, 9, 3))
+    k = r.standard_normal((1, 2, 9, 3))
+    v = r.standard_normal((1, 2, 9, 3))
+    for left, right in ((2, 0), (1, 3), (0, 2)):
+        o, lse, p = impl(q, k, v, 0.5, False, None, return_p=True, window=(left, right))
+        for i in range(9):
+            allowed = np.array([i - left <= j <= i + right for j in range(9)])
+            assert np.all(p[0, :, i, ~allowed] == 0.0), "keys outside the window have zero weight"
+            assert np.all(p[0, :, i, allowed] > 0.0), "keys inside the window have positive weight"
+            _close(p[0, :, i].sum(axis=-1), np.ones(2), 1e-14, "window rows of P sum to 1")
+
+
+WINDOW_PINS = [pin_window_brute_force, pin_window_diagonal, pin_window_reductions,
+               pin_window_probabilities]

@@ -87,3 +87,67 @@ def test_unmutated_copy_passes_every_pin():
     impl = make_mutant("none")
     for pin in ALL_PINS:
         pin(impl)
+
+
+# ---- planted mistakes in the sliding-window mask, each of which must fail a window pin
+from oracle_pins import WINDOW_PINS  # noqa: E402
+
+
+def make_window_mutant(kind):
+    def impl(q, k, v, scale, causal=False, kv_seqlens=None, return_p=False, window=None):
+        q = np.asarray(q, float); k = np.asarray(k, float); v = np.asarray(v, float)
+        bsz, heads, nq, d = q.shape
+        nk = k.shape[2]
+        o = np.zeros((bsz, heads, nq, v.shape[3])); lse = np.zeros((bsz, heads, nq))
+        pp = np.zeros((bsz, heads, nq, nk))
+        left, right = (-1, -1) if window is None else window
+        if kind == "window_swapped":
+            left, right = right, left
+        for b in range(bsz):
+            L = nk if kv_seqlens is None else min(max(int(kv_seqlens[b]), 0), nk)
+            j = np.arange(nk)[None, :]
+            i = np.arange(nq)[:, None] + (1 if kind == "window_shifted" else 0)
+            ok = np.broadcast_to(j < L, (nq, nk)).copy()
+            if causal:
+                ok &= j <= np.arange(nq)[:, None]
+            if left >= 0:
+                ok &= (j > i - left) if kind == "window_left_strict" else (j >= i - left)
+            if right >= 0 and kind != "window_right_ignored":
+                ok &= j <= i + right
+            for h in range(heads):
+                s = np.where(ok, scale * (q[b, h] @ k[b, h].T), -np.inf)
+                has = ok.any(axis=1)
+                m = np.where(has, s.max(axis=1, initial=-np.inf), 0.0)
+                e = np.where(ok, np.exp(s - m[:, None]), 0.0)
+                l = e.sum(axis=1)
+                p = np.where(has[:, None], e / np.where(l > 0, l, 1.0)[:, None], 0.0)
+                out = p @ v[b, h]
+                with np.errstate(divide="ignore"):
+                    lv = np.where(has, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+                o[b, h], lse[b, h], pp[b, h] = out, lv, p
+        if return_p:
+            return o, lse, pp
+        return o, lse
+    return impl
+
+
+WINDOW_MUTANTS = ["window_left_strict", "window_right_ignored", "window_swapped", "window_shifted"]
+
+
+@pytest.mark.parametrize("kind", WINDOW_MUTANTS)
+def test_window_mutant_fails_some_pin(kind):
+    impl = make_window_mutant(kind)
+    failed = []
+    for pin in WINDOW_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(impl)
+        except (AssertionError, FloatingPointError, ValueError, OverflowError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {kind} passed every window pin"
+
+
+def test_unmutated_window_copy_passes_every_pin():
+    impl = make_window_mutant("none")
+    for pin in WINDOW_PINS:
+        pin(impl)

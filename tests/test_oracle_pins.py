@@ -5,14 +5,15 @@ import pytest
 
 from oracle import attention_fwd, bf16_bits_to_f64
 
-from oracle_pins import ALL_PINS
+from oracle_pins import ALL_PINS, WINDOW_PINS
 
 
-def oracle_impl(q, k, v, scale, causal=False, kv_seqlens=None, return_p=False):
-    return attention_fwd(q, k, v, scale, causal=causal, kv_seqlens=kv_seqlens, return_p=return_p)
+def oracle_impl(q, k, v, scale, causal=False, kv_seqlens=None, return_p=False, window=None):
+    return attention_fwd(q, k, v, scale, causal=causal, kv_seqlens=kv_seqlens, return_p=return_p,
+                         window=window)
 
 
-@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", ALL_PINS + WINDOW_PINS, ids=lambda f: f.__name__)
 def test_oracle_pin(pin):
     pin(oracle_impl)
 
