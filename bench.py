@@ -11,7 +11,10 @@ the same run and reported under "decode". Prints ONE JSON line.
 
 The standard (materialising) algorithm, fa_std_fwd, is timed on the three prefill workloads and
 reported under "standard_attention" with its speedup ratio against fa_fwd (the pages' headline
-comparison) and the HBM roofline of the whole call on the default workload.
+comparison) and the HBM roofline of the whole call on the default workload. The generalised masks
+are timed on the long workload's shape and reported under "masks": a causal sliding window of
+4096 keys (fa_fwd_window) and the same batch packed as variable-length sequences
+(fa_fwd_varlen), with FLOPs counted over the allowed (query, key) pairs.
 
 FLOPs are counted as 4*B*H*Nq*Nk*d, halved for causal masking. Decode bytes are the algorithmic
 HBM bytes: Q, the valid K and V rows, O and lse.
@@ -193,6 +196,47 @@ def bench_standard(fa, configs, inputs, torch, dev, steps, warmup, main_name):
     return out
 
 
+def bench_masks(fa, configs, inputs, torch, dev, steps, warmup):
+    """Sliding window and packed sequences on the 16K causal shape."""
+    w = configs.LONG_CAUSAL_16K
+    q, k, v, _ = inputs.make(w, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    out = {"workload": w.name, "unit": "TFLOP/s", "peak": PEAK_MFMA_BF16_TFLOPS}
+    W = 4096
+    pairs = int(np.minimum(np.arange(1, w.Nq + 1), W).sum())
+    flops = 4 * w.B * w.H * pairs * w.d
+
+    def win():
+        fa.fa_fwd_window(q, k, v, o, lse, w.B, w.H, w.Nq, w.Nk, w.d, w.scale, W - 1, 0, None, None)
+
+    t, per = time_launches(win, steps, warmup, torch)
+    avg = float(np.mean(per))
+    out["sliding_window"] = {"window": [W - 1, 0], "ms_per_step": round(t / steps * 1e3, 4),
+                             "allowed_pairs_per_head": pairs, "counted_flops": flops,
+                             "value": round(flops * steps / t / 1e12, 2),
+                             "frac": round(flops / avg / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4)}
+    H, T = w.H, w.B * w.Nq
+    qp = q.permute(1, 0, 2, 3).reshape(H, T, w.d).contiguous()
+    kp = k.permute(1, 0, 2, 3).reshape(H, T, w.d).contiguous()
+    vp = v.permute(1, 0, 2, 3).reshape(H, T, w.d).contiguous()
+    del q, k, v, o
+    op = torch.empty_like(qp)
+    lp = torch.empty((H, T), dtype=torch.float32, device=dev)
+    cu = torch.arange(0, T + 1, w.Nq, dtype=torch.int32, device=dev)
+
+    def packed():
+        fa.fa_fwd_varlen(qp, kp, vp, op, lp, w.B, H, T, T, w.Nq, w.d, w.scale, -1, 0, cu, cu, None)
+
+    t, per = time_launches(packed, steps, warmup, torch)
+    avg = float(np.mean(per))
+    fl = w.counted_flops()
+    out["packed_causal"] = {"sequences": w.B, "layout": "[H][T][d]", "ms_per_step": round(t / steps * 1e3, 4),
+                            "counted_flops": fl, "value": round(fl * steps / t / 1e12, 2),
+                            "frac": round(fl / avg / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4)}
+    return out
+
+
 def decode_bytes(w, lens) -> int:
     per_key = 2 * w.d * 2                      # one K row and one V row, bf16
     per_bh = 2 * w.d * 2 + 4                   # Q and O rows (bf16) and lse (fp32)
@@ -208,6 +252,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-standard", action="store_true",
                     help="skip the standard-algorithm comparison (fa_std_fwd)")
+    ap.add_argument("--no-masks", action="store_true",
+                    help="skip the sliding-window and packed-sequence timings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -299,6 +345,9 @@ def main():
                          "traffic": traffic_from_profile("decode_split_kernel", wd.name, sha)},
         }
         del dq, dk, dv, do
+
+    if not args.no_masks:
+        result["masks"] = bench_masks(fa, configs, inputs, torch, dev, args.steps, args.warmup)
 
     if not args.no_standard and w.Nq > 1 and w.dtype == "bf16":
         result["standard_attention"] = bench_standard(fa, configs, inputs, torch, dev, args.steps,

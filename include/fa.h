@@ -68,6 +68,42 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                const int32_t* kv_seqlens, void* stream);
 
 /*
+ * fa_fwd_window -- fa_fwd with a sliding-window mask instead of the causal flag: key j is
+ * allowed for query i iff j < L_b, j >= i - window_left (if window_left >= 0) and
+ * j <= i + window_right (if window_right >= 0); -1 means no limit on that side. Query i sits at
+ * key position i, the alignment of the causal mask, so (-1, 0) is the causal mask, (W-1, 0) a
+ * causal window of the W most recent keys, (-1, -1) no mask. Sliding windows are among the
+ * masks the pages name beside causal masks and variable-length batches as making tile edges
+ * irregular (page "FlashAttention：把注意力从公式写成数据流", section "精度、掩码和边界情况").
+ * Tiles outside every row's window are neither read nor computed.
+ *   Same arguments and layouts as fa_fwd, with window_left, window_right >= -1 and, when either
+ *   is >= 0, Nq == Nk (else FA_ERR_UNSUPPORTED). Every Nq (also 1) runs the tiled kernel.
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Nq, int Nk, int d, float scale, int window_left,
+                  int window_right, const int32_t* kv_seqlens, void* stream);
+
+/*
+ * fa_fwd_varlen -- packed variable-length batch: B sequences of different lengths stored back
+ * to back, without padding (the "变长 batch" of the same section). Sequence b holds query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1.
+ * Within a sequence the mask is that of fa_fwd_window (query i at key position i of its own
+ * sequence; use window (-1, 0) for causal, (-1, -1) for none).
+ *   Layout (head-major, rows of d contiguous):
+ *     q, o : [H][total_q][d]   k, v : [H][total_k][d]   lse : [H][total_q] fp32
+ *   cu_seqlens_q, cu_seqlens_k : device int32 [B+1], non-decreasing, starting at 0 and ending at
+ *     total_q / total_k. Offsets are clamped to [0, total] on the device, so no access leaves the
+ *     tensors even for malformed offsets.
+ *   max_seqlen_q >= the longest query sequence (sets the grid; rows past it are not computed).
+ *   B, H, total_q, total_k, max_seqlen_q >= 0; d in {64, 128}; one head's rows of q, o, k or v
+ *   below 2^31 bytes. B*H*total_q == 0 or max_seqlen_q == 0 is a valid no-op.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int total_q, int total_k, int max_seqlen_q, int d, float scale,
+                  int window_left, int window_right, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, void* stream);
+
+/*
  * fa_std_fwd -- the same bf16 operation computed by the standard, materialising algorithm, the
  * baseline the tiled path is measured against (page "FlashAttention：把注意力从公式写成数据流",
  * opening paragraph: S = Q K^T is written to device memory, read back for the softmax, and P is

@@ -9,6 +9,10 @@ Entry points mirror the C ABI in ``include/fa.h``:
 
 * ``fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, stream)`` -- bf16
 * ``fa_fwd_f32(...)``                                                          -- fp32
+* ``fa_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, d, scale, window_left, window_right,
+  kv_seqlens, stream)`` -- bf16, sliding-window mask
+* ``fa_fwd_varlen(q, k, v, o, lse, B, H, total_q, total_k, max_seqlen_q, d, scale, window_left,
+  window_right, cu_seqlens_q, cu_seqlens_k, stream)`` -- bf16, packed variable-length batch
 * ``fa_std_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, workspace,
   workspace_bytes, stream)`` -- bf16, standard (materialising) algorithm, the baseline
 * ``fa_std_workspace_bytes(B, H, Nq, Nk)``
@@ -16,7 +20,9 @@ Entry points mirror the C ABI in ``include/fa.h``:
 
 Pointer arguments accept a torch tensor (its ``data_ptr()``), an int address or None; ``stream``
 accepts a ``torch.cuda.Stream``, an int handle or None (the current torch stream).
-``attention(q, k, v, ...)`` allocates O and lse with torch and calls the right entry point;
+``attention(q, k, v, ...)`` allocates O and lse with torch and calls the right entry point
+(``window=(left, right)`` selects ``fa_fwd_window``); ``varlen_attention`` does the same for
+packed sequences;
 ``standard_attention(q, k, v, ...)`` does the same for ``fa_std_fwd`` (bf16 only), allocating
 its workspace with torch unless one is passed.
 """
@@ -28,9 +34,9 @@ import math
 import os
 from typing import Optional, Tuple
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_std_fwd", "fa_std_workspace_bytes",
-           "fa_status_string", "fa_last_error", "attention", "standard_attention", "library_path",
-           "load_library"]
+__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_window", "fa_fwd_varlen", "fa_std_fwd",
+           "fa_std_workspace_bytes", "fa_status_string", "fa_last_error", "attention",
+           "varlen_attention", "standard_attention", "library_path", "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfa.so")
@@ -68,6 +74,10 @@ def load_library():
         fn = getattr(lib, name)
         fn.argtypes = sig
         fn.restype = ci
+    lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, ci, vp, vp]
+    lib.fa_fwd_window.restype = ci
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, vp, vp, vp]
+    lib.fa_fwd_varlen.restype = ci
     lib.fa_std_fwd.argtypes = sig[:13] + [vp, ctypes.c_size_t, vp]
     lib.fa_std_fwd.restype = ci
     lib.fa_std_workspace_bytes.argtypes = [ci, ci, ci, ci]
@@ -122,6 +132,62 @@ def fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens=None, str
 def fa_fwd_f32(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens=None, stream=None) -> None:
     """fp32 forward; see include/fa.h for the contract."""
     _call("fa_fwd_f32", q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, stream)
+
+
+def _raise(st):
+    if st != FA_OK:
+        raise FaError(st, f"{fa_status_string(st)} ({fa_last_error()})")
+
+
+def fa_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, d, scale, window_left, window_right,
+                  kv_seqlens=None, stream=None) -> None:
+    """bf16 forward with a sliding-window mask; see include/fa.h for the contract."""
+    lib = load_library()
+    _raise(lib.fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq),
+                             int(Nk), int(d), float(scale), int(window_left), int(window_right),
+                             _ptr(kv_seqlens), _stream(stream)))
+
+
+def fa_fwd_varlen(q, k, v, o, lse, B, H, total_q, total_k, max_seqlen_q, d, scale, window_left,
+                  window_right, cu_seqlens_q, cu_seqlens_k, stream=None) -> None:
+    """bf16 forward over a packed variable-length batch; see include/fa.h for the contract."""
+    lib = load_library()
+    _raise(lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                             int(total_q), int(total_k), int(max_seqlen_q), int(d), float(scale),
+                             int(window_left), int(window_right), _ptr(cu_seqlens_q),
+                             _ptr(cu_seqlens_k), _stream(stream)))
+
+
+def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                     scale: Optional[float] = None, window=(-1, -1), out=None, lse=None,
+                     stream=None) -> Tuple["object", "object"]:
+    """O [H, Tq, d] and lse [H, Tq] for packed bf16 q [H, Tq, d], k, v [H, Tk, d]."""
+    import torch
+
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [H, T, d]")
+    H, Tq, d = q.shape
+    Tk = k.shape[1]
+    if tuple(k.shape) != (H, Tk, d) or tuple(v.shape) != (H, Tk, d):
+        raise ValueError("k and v must be [H, Tk, d] matching q")
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous bfloat16 device tensors")
+    for c in (cu_seqlens_q, cu_seqlens_k):
+        if c.dtype != torch.int32 or not c.is_cuda:
+            raise ValueError("cu_seqlens must be int32 device tensors")
+    B = cu_seqlens_q.numel() - 1
+    if B < 0 or cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B + 1 entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
+    fa_fwd_varlen(q, k, v, out, lse, B, H, Tq, Tk, max_seqlen_q, d, scale, window[0], window[1],
+                  cu_seqlens_q, cu_seqlens_k, stream)
+    return out, lse
 
 
 def fa_std_workspace_bytes(B, H, Nq, Nk) -> int:
@@ -183,8 +249,10 @@ def standard_attention(q, k, v, scale: Optional[float] = None, causal: bool = Fa
 
 
 def attention(q, k, v, scale: Optional[float] = None, causal: bool = False, kv_seqlens=None,
-              out=None, lse=None, stream=None) -> Tuple["object", "object"]:
-    """O, lse for device tensors q [B,H,Nq,d] and k, v [B,H,Nk,d] (bf16 or fp32, contiguous)."""
+              out=None, lse=None, stream=None, window=None) -> Tuple["object", "object"]:
+    """O, lse for device tensors q [B,H,Nq,d] and k, v [B,H,Nk,d] (bf16 or fp32, contiguous).
+
+    window=(left, right) applies a sliding-window mask (bf16 only, not together with causal)."""
     import torch
 
     B, H, Nq, Nk, d = _check_qkv(q, k, v, kv_seqlens, (torch.bfloat16, torch.float32))
@@ -194,6 +262,12 @@ def attention(q, k, v, scale: Optional[float] = None, causal: bool = False, kv_s
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if window is not None:
+        if causal or q.dtype != torch.bfloat16:
+            raise ValueError("window needs bf16 inputs and causal=False (use window (-1, 0))")
+        fa_fwd_window(q, k, v, out, lse, B, H, Nq, Nk, d, scale, window[0], window[1], kv_seqlens,
+                      stream)
+        return out, lse
     fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
     fn(q, k, v, out, lse, B, H, Nq, Nk, d, scale, int(bool(causal)), kv_seqlens, stream)
     return out, lse

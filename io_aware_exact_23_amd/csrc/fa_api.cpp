@@ -12,10 +12,12 @@
 namespace fa {
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);
 hipError_t launch_prefill_bf16_pp(const PrefillParams& p, int d, hipStream_t stream);
+hipError_t launch_prefill_bf16_general(const PrefillParams& p, int d, int max_nq, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_standard(const StandardParams& p, int d, hipStream_t stream);
 int prefill_bf16_rows_per_wg(int d);
+int prefill_bf16_pp_rows_per_wg();
 constexpr int kPrefillLongNq = 2048;  // query rows from which the 8-wave prefill kernel is used
 int decode_chunk();
 }  // namespace fa
@@ -148,6 +150,73 @@ extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float*
   if (n_wg > std::numeric_limits<int32_t>::max()) return fail(FA_ERR_UNSUPPORTED, "grid too large");
   fa::PrefillParams p = prefill_params(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_seqlens);
   hipError_t e = fa::launch_prefill_f32(p, d, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "prefill launch");
+  return FA_OK;
+}
+
+namespace {
+int check_window(int left, int right) {
+  if (left < -1 || right < -1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "window_left and window_right must be >= -1");
+  return FA_OK;
+}
+}  // namespace
+
+extern "C" int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int Nq, int Nk, int d, float scale, int window_left,
+                             int window_right, const int32_t* kv_seqlens, void* stream) {
+  const bool bounded = window_left >= 0 || window_right >= 0;
+  int st = check_window(window_left, window_right);
+  if (st != FA_OK) return st;
+  st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, 0, kv_seqlens);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  if (bounded && Nq != Nk) return fail(FA_ERR_UNSUPPORTED, "a bounded window needs Nq == Nk");
+  const int bm = fa::prefill_bf16_pp_rows_per_wg();
+  if ((int64_t)B * H * ((Nq + bm - 1) / bm) > std::numeric_limits<int32_t>::max())
+    return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  fa::PrefillParams p = prefill_params(q, k, v, o, lse, B, H, Nq, Nk, scale, 0, kv_seqlens);
+  p.win_left = window_left;
+  p.win_right = window_right;
+  hipError_t e = fa::launch_prefill_bf16_general(p, d, Nq, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "prefill launch");
+  return FA_OK;
+}
+
+extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int total_q, int total_k, int max_seqlen_q, int d,
+                             float scale, int window_left, int window_right,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* stream) {
+  g_last_error[0] = '\0';
+  int st = check_window(window_left, window_right);
+  if (st != FA_OK) return st;
+  if (B < 0 || H < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "B, H, total_q, total_k, max_seqlen_q must be >= 0");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d must be 64 or 128");
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "scale must be finite");
+  const int64_t bh = (int64_t)B * H;
+  if (bh == 0 || total_q == 0 || max_seqlen_q == 0) return FA_OK;
+  if (!q || !o || !lse || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(FA_ERR_INVALID_ARGUMENT, "q, o, lse and the cu_seqlens arrays must be non-null");
+  if (total_k > 0 && (!k || !v)) return fail(FA_ERR_INVALID_ARGUMENT, "k and v must be non-null");
+  if (!aligned(q, 16) || !aligned(o, 16) || (k && !aligned(k, 16)) || (v && !aligned(v, 16)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "q, k, v and o must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return fail(FA_ERR_INVALID_ARGUMENT, "lse and the cu_seqlens arrays must be 4-byte aligned");
+  if ((int64_t)total_q * d * 2 > std::numeric_limits<int32_t>::max() ||
+      (int64_t)total_k * d * 2 > std::numeric_limits<int32_t>::max())
+    return fail(FA_ERR_UNSUPPORTED, "one head's packed rows must stay below 2^31 bytes");
+  const int bm = fa::prefill_bf16_pp_rows_per_wg();
+  if (bh * ((max_seqlen_q + bm - 1) / bm) > std::numeric_limits<int32_t>::max())
+    return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  fa::PrefillParams p = prefill_params(q, k, v, o, lse, B, H, 0, 0, scale, 0, nullptr);
+  p.win_left = window_left;
+  p.win_right = window_right;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.Tq = total_q;
+  p.Tk = total_k;
+  hipError_t e = fa::launch_prefill_bf16_general(p, d, max_seqlen_q, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail_hip(e, "prefill launch");
   return FA_OK;
 }

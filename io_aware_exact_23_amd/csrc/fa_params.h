@@ -18,6 +18,11 @@ struct PrefillParams {
   int causal;
   int n_qtiles;   // ceil(Nq / BM)
   int n_tiles;    // B * H * n_qtiles (the grid size)
+  // Generalised masks and layouts (the window / packed-sequence entry points only).
+  int win_left, win_right;    // key j allowed for query i iff i-left <= j <= i+right; -1: no limit
+  const int32_t* cu_q;        // packed sequences: [B+1] row offsets of each sequence, or nullptr
+  const int32_t* cu_k;        //   (then q, o are [H][Tq][D], k, v [H][Tk][D], lse [H][Tq])
+  int Tq, Tk;                 // packed sequences: rows per head
 };
 
 // Split-KV decode (Nq == 1): one workgroup per (split, h, b), then a combine pass.

@@ -104,7 +104,11 @@ __device__ __forceinline__ void wg_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D>
+// kGen = false: the fa_fwd masks (causal, key lengths) on [B][H][N][D] tensors. kGen = true:
+// sliding windows (left, right) and, with cu_q / cu_k, packed sequences; the loop structure gains
+// a masked prefix (tiles that reach below the window of the workgroup's last row) and the
+// K/V stream starts at the first tile any row of the workgroup may see.
+template <int D, bool kGen>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_pp_kernel(PrefillParams p) {
   using C = PrefillPPCfg<D>;
@@ -125,26 +129,61 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
   const int tile = xcd_remap(blockIdx.x, p.n_tiles);
   const int bh = tile / p.n_qtiles;
   int qt = tile - bh * p.n_qtiles;
-  if (p.causal) qt = p.n_qtiles - 1 - qt;
+  const bool right_bounded = kGen ? p.win_right >= 0 : p.causal != 0;
+  if (right_bounded) qt = p.n_qtiles - 1 - qt;
   const int b = bh / p.H;
   const int q0 = qt * C::kBM;
-  const int L = seq_len(p.kv_seqlens, b, p.Nk);
-  int kend = L;
-  if (p.causal) kend = min(kend, min(q0 + C::kBM, p.Nq));
-  const int n = kend > 0 ? (kend + C::kBN - 1) / C::kBN : 0;  // key tiles of this workgroup
 
-  const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + (size_t)bh * p.Nq * D;
-  const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + (size_t)bh * p.Nk * D;
-  const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + (size_t)bh * p.Nk * D;
-  // Range-checked views: rows >= Nq of Q and keys >= kend of K and V read as zeros, so the loads
-  // need no branches, masked keys can never bring NaN or Inf into the products, and tiles past
-  // this workgroup's last one cost no memory traffic.
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, (uint32_t)p.Nq * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kg, (uint32_t)kend * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vg, (uint32_t)kend * C::kRowBytes);
+  // Sequence geometry: this (b, h)'s query rows [0, Nq) and valid keys [0, L), their base rows.
+  int Nq = p.Nq, L;
+  const uint16_t *Qg, *Kg, *Vg;
+  uint16_t* Og;
+  float* lseg;
+  if (kGen && p.cu_q) {
+    const int h = bh - b * p.H;
+    const int qr0 = clampi(p.cu_q[b], 0, p.Tq), qr1 = clampi(p.cu_q[b + 1], qr0, p.Tq);
+    const int kr0 = clampi(p.cu_k[b], 0, p.Tk), kr1 = clampi(p.cu_k[b + 1], kr0, p.Tk);
+    Nq = qr1 - qr0;
+    L = kr1 - kr0;
+    const size_t qrow = (size_t)h * p.Tq + qr0, krow = (size_t)h * p.Tk + kr0;
+    Qg = static_cast<const uint16_t*>(p.q) + qrow * D;
+    Og = static_cast<uint16_t*>(p.o) + qrow * D;
+    lseg = p.lse + qrow;
+    Kg = static_cast<const uint16_t*>(p.k) + krow * D;
+    Vg = static_cast<const uint16_t*>(p.v) + krow * D;
+  } else {
+    L = seq_len(p.kv_seqlens, b, p.Nk);
+    Qg = static_cast<const uint16_t*>(p.q) + (size_t)bh * p.Nq * D;
+    Og = static_cast<uint16_t*>(p.o) + (size_t)bh * p.Nq * D;
+    lseg = p.lse + (size_t)bh * p.Nq;
+    Kg = static_cast<const uint16_t*>(p.k) + (size_t)bh * p.Nk * D;
+    Vg = static_cast<const uint16_t*>(p.v) + (size_t)bh * p.Nk * D;
+  }
+  if (kGen && q0 >= Nq) return;  // a query tile past this packed sequence (uniform per workgroup)
+
+  // Key range of the workgroup: tiles i_lo .. n-1 (n exclusive); kend is one past its last key.
+  // Without a window i_lo = 0. With one, the stream starts at the first tile any of its rows may
+  // see, and the buffer views below start there too, so keys before it are never read.
+  int i_lo = 0, kend = L;
+  if constexpr (kGen) {
+    const int q_last = min(q0 + C::kBM, Nq) - 1;
+    if (p.win_left >= 0) i_lo = max(0, q0 - p.win_left) / C::kBN;
+    if (p.win_right >= 0) kend = min(kend, q_last + p.win_right + 1);
+    kend = max(kend, i_lo * C::kBN);
+  } else {
+    if (p.causal) kend = min(kend, min(q0 + C::kBM, Nq));
+  }
+  const int n = kend > 0 ? (kend + C::kBN - 1) / C::kBN : 0;  // key tiles end (exclusive)
+  const int kfirst = i_lo * C::kBN;
+
+  // Range-checked views: rows >= Nq of Q and keys outside [kfirst, kend) of K and V read as
+  // zeros, so the loads need no branches, masked keys can never bring NaN or Inf into the
+  // products, and tiles past this workgroup's last one cost no memory traffic.
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, (uint32_t)Nq * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kg + (size_t)kfirst * D, (uint32_t)(kend - kfirst) * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vg + (size_t)kfirst * D, (uint32_t)(kend - kfirst) * C::kRowBytes);
 
   const int qw0 = q0 + rblk * C::kQW;
-  const int qw_last = min(qw0 + C::kQW, p.Nq) - 1;  // < qw0 when the wave has no rows
   // Scores are handled in base-2 units t = c * (q.k). For c < 0 the kernel negates its copy of Q
   // (a sign flip, exact in bf16 and in every product and sum) and uses -c, so below c > 0 always
   // and the running extreme is always a maximum.
@@ -182,8 +221,9 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
     koff[it] = (uint32_t)(pp_k_perm(row) * C::kRowBytes + ((slot ^ (row % C::kNch)) << 4));
     voff[it] = (uint32_t)(row * C::kRowBytes + ((slot ^ (4 * (row % (C::kNch / 4)))) << 4));
   }
-  // Unit u = (K tile u, V tile u - 1). V tile -1 and K tile n lie outside the buffer range and
-  // read as zeros (the unsigned offset of tile -1 wraps far past any valid range).
+  // Unit u = (K tile i_lo + u, V tile i_lo + u - 1), offsets relative to the views' start. V tile
+  // i_lo - 1 and K tile n lie outside the buffer range and read as zeros (the unsigned offset of
+  // tile -1 wraps far past any valid range).
   auto issue_unit = [&](int u, char* dst) __attribute__((always_inline)) {
     const uint32_t kbase = (uint32_t)u * C::kTileBytes;
     const uint32_t vbase = (uint32_t)(u - 1) * C::kTileBytes;
@@ -255,21 +295,33 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
   // an allowed key in the tile.
   auto exponent_args = [&](auto mask_tag, int k0, float moff) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
-    int rem = 64;
+    int rem = 64, lo = 0;  // allowed offsets: lo <= off < rem
     if constexpr (kMask) {
       const int qi = qw0 + r32;
-      rem = (p.causal ? min(L, qi + 1) : L) - (k0 + 8 * g);
-      if (qi >= p.Nq) rem = 0;
+      const int kl = k0 + 8 * g;
+      if constexpr (kGen) {
+        // Window of row qi: keys max(0, qi - left) .. min(L, qi + right + 1) - 1.
+        int hi = L;
+        if (p.win_right >= 0) hi = min(hi, qi + p.win_right + 1);
+        rem = hi - kl;
+        if (p.win_left >= 0) lo = qi - p.win_left - kl;
+      } else {
+        rem = (p.causal ? min(L, qi + 1) : L) - kl;
+      }
+      if (qi >= Nq) rem = 0;
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float t = fmaf(sacc[kb][e], c, -moff);
-        if constexpr (kMask) sacc[kb][e] = (kb * 32 + ((e >> 3) << 4) + (e & 7) < rem) ? t : -kInf;
+        const int off = kb * 32 + ((e >> 3) << 4) + (e & 7);
+        if constexpr (kMask && kGen) sacc[kb][e] = (off < rem && off >= lo) ? t : -kInf;
+        else if constexpr (kMask) sacc[kb][e] = (off < rem) ? t : -kInf;
         else sacc[kb][e] = t;
       }
-    return rem > 0;
+    // Whether [lo, rem) meets this lane's offsets 0..55; an over-estimate only costs a rescale.
+    return rem > 0 && rem > lo && lo < 56;
   };
 
   // ---- Matrix phase i: one software-pipelined sequence of kNM MFMAs, S_i = K_i Q^T and then
@@ -393,17 +445,18 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
     if (pr) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto interval = [&](auto order_tag, auto mask_tag, int i, const char* unit, int hs, char* ahead)
+  auto interval = [&](auto order_tag, auto mask_tag, int t, const char* unit, int hs, char* ahead)
       __attribute__((always_inline)) {
     constexpr bool kMatrixFirst = decltype(order_tag)::value;
+    const int i = i_lo + t;  // key tile of this interval (t counts from the first one)
     if constexpr (kMatrixFirst) {
       matrix_phase(unit, hs);
-      issue_unit(i + 3, ahead);
+      issue_unit(t + 3, ahead);
       set_prio(1);
       softmax_phase(mask_tag, i * C::kBN);
       set_prio(0);
     } else {
-      issue_unit(i + 3, ahead);
+      issue_unit(t + 3, ahead);
       set_prio(1);
       softmax_phase(mask_tag, (i - 1) * C::kBN);
       set_prio(0);
@@ -412,32 +465,55 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
     wait_vmcnt<2 * C::kLoadsPerUnit>();
     wg_barrier();
   };
-  // Two loops, each with a single code path (a branch per tile would make the compiler copy the
-  // accumulators at every join): tiles 0 .. i_mask-1 need no mask for any wave of the workgroup;
-  // tiles i_mask .. n take the masked variant, a no-op mask on tiles that happen to be whole.
-  // Tiles needing a mask: the ragged tail (key k0 + 63 >= L), and when causal those reaching past
-  // the workgroup's first row (k0 + 63 > q0); tile n is fully masked. i_mask is rounded down to
-  // a multiple of the slot count, so both loops start on slot 0. Both loops are unrolled by the
-  // slot count so every LDS access names its slot array; the guards are nested so that the
-  // compiler's wait-count tracking sees only the paths that can happen.
-  int i_mask = min(n, L / C::kBN);
-  if (p.causal) i_mask = min(i_mask, q0 / C::kBN);
-  i_mask &= ~3;
+  // Loops with a single code path each (a branch per tile would make the compiler copy the
+  // accumulators at every join), over t = i - i_lo = 0 .. n - i_lo (interval n - i_lo only
+  // completes the last tile; its own tile is fully masked). Tiles i_u0 .. i_u1 - 1 need no mask
+  // for any row of the workgroup; the others take the masked variant, a no-op mask on tiles that
+  // happen to be whole. Needing a mask: the ragged tail (key k0 + 63 >= L); tiles reaching past
+  // the workgroup's first row when causal (k0 + 63 > q0), or past q0 + right with a window; and,
+  // with a window's left limit, tiles starting below q_last - left. The loops are unrolled by the
+  // slot count (slot = t % 4) so every LDS access names its slot array; the guards of the last
+  // loop are nested so that the compiler's wait-count tracking sees only the paths that happen.
+  const int t_end = n - i_lo;
+  int t_u0 = 0, t_u1;
+  if constexpr (kGen) {
+    const int q_last = min(q0 + C::kBM, Nq) - 1;
+    int hi_min = L;  // every row of the workgroup may see keys below hi_min ...
+    if (p.win_right >= 0) hi_min = min(hi_min, q0 + p.win_right + 1);
+    int lo_max = 0;  // ... and at or above lo_max
+    if (p.win_left >= 0) lo_max = max(0, q_last - p.win_left);
+    t_u0 = max(0, (lo_max + C::kBN - 1) / C::kBN - i_lo);
+    t_u1 = min(t_end, hi_min / C::kBN - i_lo);
+  } else {
+    t_u1 = min(n, L / C::kBN);
+    if (p.causal) t_u1 = min(t_u1, q0 / C::kBN);
+  }
+  // Interval t runs group 0's softmax of tile t but group 1's of tile t - 1, so an unmasked
+  // interval needs both tiles unmasked: the masked prefix covers t <= t_u0 whenever t_u0 > 0.
+  const int t_pre = t_u0 > 0 ? t_u0 + 1 : 0;
   auto run = [&](auto order_tag) __attribute__((always_inline)) {
-    int i = 0;
-    for (; i < i_mask; i += 4) {
-      interval(order_tag, std::false_type{}, i, slot0, 0, slot3);
-      interval(order_tag, std::false_type{}, i + 1, slot1, 0, slot0);
-      interval(order_tag, std::false_type{}, i + 2, slot2, 1, slot1);
-      interval(order_tag, std::false_type{}, i + 3, slot3, 1, slot2);
+    int t = 0;
+    if constexpr (kGen) {
+      for (; t < t_pre && t + 3 <= t_end; t += 4) {
+        interval(order_tag, std::true_type{}, t, slot0, 0, slot3);
+        interval(order_tag, std::true_type{}, t + 1, slot1, 0, slot0);
+        interval(order_tag, std::true_type{}, t + 2, slot2, 1, slot1);
+        interval(order_tag, std::true_type{}, t + 3, slot3, 1, slot2);
+      }
     }
-    for (; i <= n; i += 4) {
-      interval(order_tag, std::true_type{}, i, slot0, 0, slot3);
-      if (i + 1 <= n) {
-        interval(order_tag, std::true_type{}, i + 1, slot1, 0, slot0);
-        if (i + 2 <= n) {
-          interval(order_tag, std::true_type{}, i + 2, slot2, 1, slot1);
-          if (i + 3 <= n) interval(order_tag, std::true_type{}, i + 3, slot3, 1, slot2);
+    for (; t + 4 <= t_u1; t += 4) {
+      interval(order_tag, std::false_type{}, t, slot0, 0, slot3);
+      interval(order_tag, std::false_type{}, t + 1, slot1, 0, slot0);
+      interval(order_tag, std::false_type{}, t + 2, slot2, 1, slot1);
+      interval(order_tag, std::false_type{}, t + 3, slot3, 1, slot2);
+    }
+    for (; t <= t_end; t += 4) {
+      interval(order_tag, std::true_type{}, t, slot0, 0, slot3);
+      if (t + 1 <= t_end) {
+        interval(order_tag, std::true_type{}, t + 1, slot1, 0, slot0);
+        if (t + 2 <= t_end) {
+          interval(order_tag, std::true_type{}, t + 2, slot2, 1, slot1);
+          if (t + 3 <= t_end) interval(order_tag, std::true_type{}, t + 3, slot3, 1, slot2);
         }
       }
     }
@@ -459,11 +535,9 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
   wait_vmcnt<0>();  // nothing may still write into LDS when the workgroup ends
 
   // Epilogue: O = O^T / l, lse = ln 2 * (m + log2 l); a row with no allowed key gets 0 and -inf.
-  uint16_t* Og = static_cast<uint16_t*>(p.o) + (size_t)bh * p.Nq * D;
-  float* lseg = p.lse + (size_t)bh * p.Nq;
   const float lt = pair32_sum(lsum);
   const int qi = qw0 + r32;
-  if (qi < p.Nq) {
+  if (qi < Nq) {
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     if (g == 0) lseg[qi] = lt > 0.0f ? (m_used + fast_log2(lt)) * kLn2 : -kInf;
 #pragma unroll
@@ -478,21 +552,27 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
   }
 }
 
-template <int D>
-static hipError_t launch_pp(PrefillParams p, hipStream_t stream) {
+template <int D, bool kGen>
+static hipError_t launch_pp(PrefillParams p, int max_nq, hipStream_t stream) {
   using C = PrefillPPCfg<D>;
-  p.n_qtiles = (p.Nq + C::kBM - 1) / C::kBM;
+  p.n_qtiles = (max_nq + C::kBM - 1) / C::kBM;
   p.n_tiles = p.B * p.H * p.n_qtiles;
   if (p.n_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_bf16_pp_kernel<D>), dim3(p.n_tiles), dim3(C::kThreads), 0, stream, p);
+  hipLaunchKernelGGL((prefill_bf16_pp_kernel<D, kGen>), dim3(p.n_tiles), dim3(C::kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 int prefill_bf16_pp_rows_per_wg() { return PrefillPPCfg<128>::kBM; }
 
 hipError_t launch_prefill_bf16_pp(const PrefillParams& p, int d, hipStream_t stream) {
-  if (d == 64) return launch_pp<64>(p, stream);
-  return launch_pp<128>(p, stream);
+  if (d == 64) return launch_pp<64, false>(p, p.Nq, stream);
+  return launch_pp<128, false>(p, p.Nq, stream);
+}
+
+// Sliding windows and packed sequences: max_nq bounds every sequence's query count.
+hipError_t launch_prefill_bf16_general(const PrefillParams& p, int d, int max_nq, hipStream_t stream) {
+  if (d == 64) return launch_pp<64, true>(p, max_nq, stream);
+  return launch_pp<128, true>(p, max_nq, stream);
 }
 
 }  // namespace fa

@@ -29,7 +29,7 @@ def run_lib(q, k, v, scale, causal=False, lens=None):
     return o, lse
 
 
-def run_oracle(q, k, v, scale, causal=False, lens=None, rows=None, b_range=None):
+def run_oracle(q, k, v, scale, causal=False, lens=None, rows=None, b_range=None, window=None):
     """Oracle on the exact input bits; optionally restricted to query rows and a batch range."""
     lens_l = None if lens is None else [int(x) for x in lens.to("cpu").tolist()]
     bs = range(q.shape[0]) if b_range is None else b_range
@@ -39,7 +39,8 @@ def run_oracle(q, k, v, scale, causal=False, lens=None, rows=None, b_range=None)
         qb = to_f64(q[b:b + 1])
         kb = to_f64(k[b:b + 1])
         vb = to_f64(v[b:b + 1])
-        o, lse = attention_fwd(qb, kb, vb, f32(scale), causal=causal, kv_seqlens=lb, rows=rows)
+        o, lse = attention_fwd(qb, kb, vb, f32(scale), causal=causal, kv_seqlens=lb, rows=rows,
+                               window=window)
         outs.append(o)
         lses.append(lse)
     return np.concatenate(outs), np.concatenate(lses)

@@ -23,8 +23,9 @@ def declared_functions():
 
 
 def test_header_declares_the_abi():
-    assert declared_functions() == ["fa_fwd", "fa_fwd_f32", "fa_last_error", "fa_status_string",
-                                    "fa_std_fwd", "fa_std_workspace_bytes"]
+    assert declared_functions() == ["fa_fwd", "fa_fwd_f32", "fa_fwd_varlen", "fa_fwd_window",
+                                    "fa_last_error", "fa_status_string", "fa_std_fwd",
+                                    "fa_std_workspace_bytes"]
 
 
 @needs_lib
@@ -53,12 +54,20 @@ def _std(**kw):
     fa.fa_std_fwd(workspace=ws, workspace_bytes=wb, **kw)
 
 
+def _win(**kw):
+    """fa_fwd_window with the fa_fwd keyword set: causal=1 becomes the window (-1, 0)."""
+    causal = kw.pop("causal")
+    if causal not in (0, 1):
+        pytest.skip("the window entry point has no causal flag")
+    fa.fa_fwd_window(window_left=-1, window_right=0 if causal else -1, **kw)
+
+
 ENTRY = {"fa_fwd": lambda **kw: fa.fa_fwd(**kw), "fa_fwd_f32": lambda **kw: fa.fa_fwd_f32(**kw),
-         "fa_std_fwd": _std}
+         "fa_std_fwd": _std, "fa_fwd_window": _win}
 
 
 @needs_lib
-@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32", "fa_std_fwd"])
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32", "fa_std_fwd", "fa_fwd_window"])
 @pytest.mark.parametrize("args,status,needle", [
     (dict(d=96), fa.FA_ERR_UNSUPPORTED, "64 or 128"),
     (dict(d=0), fa.FA_ERR_UNSUPPORTED, "64 or 128"),
@@ -122,7 +131,7 @@ def test_standard_rejects_a_head_too_large():
 
 
 @needs_lib
-@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32", "fa_std_fwd"])
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32", "fa_std_fwd", "fa_fwd_window"])
 @pytest.mark.parametrize("args", [dict(B=0), dict(H=0), dict(Nq=0), dict(B=0, q=None, o=None, lse=None)])
 def test_empty_batch_is_a_no_op(fn, args):
     call = dict(q=A, k=A, v=A, o=A, lse=A, B=2, H=3, Nq=8, Nk=8, d=128, scale=0.1, causal=0,
@@ -137,3 +146,58 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(fa.FaError):
         fa.fa_status_string(0)
+
+
+@needs_lib
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(window_left=-2), fa.FA_ERR_INVALID_ARGUMENT, ">= -1"),
+    (dict(window_right=-5), fa.FA_ERR_INVALID_ARGUMENT, ">= -1"),
+    (dict(window_left=3, Nq=4, Nk=6), fa.FA_ERR_UNSUPPORTED, "Nq == Nk"),
+    (dict(window_right=0, Nq=4, Nk=6), fa.FA_ERR_UNSUPPORTED, "Nq == Nk"),
+])
+def test_window_argument_errors(args, status, needle):
+    call = dict(q=A, k=A, v=A, o=A, lse=A, B=2, H=3, Nq=8, Nk=8, d=64, scale=0.125, window_left=-1,
+                window_right=-1, kv_seqlens=None, stream=0)
+    call.update(args)
+    with pytest.raises(fa.FaError) as ei:
+        fa.fa_fwd_window(**call)
+    assert ei.value.status == status
+    assert needle in ei.value.message
+
+
+VARLEN = dict(q=A, k=A, v=A, o=A, lse=A, B=2, H=3, total_q=40, total_k=50, max_seqlen_q=30, d=128,
+              scale=0.1, window_left=-1, window_right=0, cu_seqlens_q=A, cu_seqlens_k=A, stream=0)
+
+
+@needs_lib
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED, "64 or 128"),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARGUMENT, ">= 0"),
+    (dict(total_k=-1), fa.FA_ERR_INVALID_ARGUMENT, ">= 0"),
+    (dict(window_left=-3), fa.FA_ERR_INVALID_ARGUMENT, ">= -1"),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARGUMENT, "finite"),
+    (dict(cu_seqlens_q=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(cu_seqlens_k=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(v=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(q=A + 8), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(cu_seqlens_k=A + 2), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(total_q=1 << 24), fa.FA_ERR_UNSUPPORTED, "2^31"),
+])
+def test_varlen_argument_errors(args, status, needle):
+    call = dict(VARLEN)
+    call.update(args)
+    with pytest.raises(fa.FaError) as ei:
+        fa.fa_fwd_varlen(**call)
+    assert ei.value.status == status
+    assert needle in ei.value.message
+
+
+@needs_lib
+@pytest.mark.parametrize("args", [dict(B=0), dict(H=0), dict(total_q=0), dict(max_seqlen_q=0),
+                                  dict(B=0, q=None, o=None, lse=None, cu_seqlens_q=None)])
+def test_varlen_empty_is_a_no_op(args):
+    call = dict(VARLEN)
+    call.update(args)
+    fa.fa_fwd_varlen(**call)
+    assert fa.fa_last_error() == ""
