@@ -42,13 +42,23 @@ m_i changes nothing in exact arithmetic; it keeps exp finite for large scores.
 
 Every quantity is fp64. Inputs arrive as fp64 arrays that hold bf16 or fp32 values exactly
 (``bf16_bits_to_f64`` converts raw bf16 bit patterns without rounding).
+
+Backward pass (``attention_bwd``). Training needs the gradients of this forward pass, and a tiled
+implementation gets them by recomputing S and P from Q, K and the saved logsumexp rather than
+storing P ([dataflow] section "用实验验证而不是背诵结论" on training needing recomputation;
+[vocus] page "[2205.14135] FlashAttention ...", section "三、FLOPs（計算能力）並非 Speedup 的主因素"
+on the extra recomputation FLOPs). The pages give no formulas, so the oracle is the plain chain
+rule of the definition above, for an upstream gradient dO, materialising P:
+  dV = P^T dO,   dP = dO V^T,   D_i = sum_j P_ij dP_ij  (= dO_i . O_i),
+  dS_ij = P_ij (dP_ij - D_i),   dQ = scale * dS K,   dK = scale * dS^T Q;
+masked pairs have P_ij = 0 and so contribute nothing; rows with no allowed key get dQ_i = 0.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["bf16_bits_to_f64", "allowed_mask", "attention_fwd", "attention_rows"]
+__all__ = ["bf16_bits_to_f64", "allowed_mask", "attention_fwd", "attention_rows", "attention_bwd"]
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -154,3 +164,35 @@ def attention_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     if return_p:
         return o, lse, p_all
     return o, lse
+
+
+def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float,
+                  causal: bool = False, kv_seqlens=None, window=None):
+    """Gradients (dQ, dK, dV) of O = attention(Q, K, V) for the upstream gradient dO.
+
+    Shapes as in attention_fwd; do has O's shape (B, H, Nq, d_v). All fp64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    bsz, heads, nq, _ = q.shape
+    nk = k.shape[2]
+    if causal and nq != nk:
+        raise ValueError("causal masking is defined here only for Nq == Nk")
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    rows = np.arange(nq)
+    for b in range(bsz):
+        length = _length(kv_seqlens, b, nk)
+        for h in range(heads):
+            _, _, p = attention_rows(q[b, h], k[b, h], v[b, h], rows, scale, causal, length,
+                                     return_p=True, window=window)
+            dv[b, h] = p.T @ do[b, h]
+            dp = do[b, h] @ v[b, h].T
+            d_i = np.sum(p * dp, axis=1)
+            ds = p * (dp - d_i[:, None])
+            dq[b, h] = float(scale) * (ds @ k[b, h])
+            dk[b, h] = float(scale) * (ds.T @ q[b, h])
+    return dq, dk, dv

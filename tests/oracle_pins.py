@@ -329,3 +329,90 @@ def pin_window_probabilities(impl):
 
 WINDOW_PINS = [pin_window_brute_force, pin_window_diagonal, pin_window_reductions,
                pin_window_probabilities]
+
+
+# ---- backward pass: impl(q, k, v, do, scale, causal=False, kv_seqlens=None, window=None)
+# returns (dq, dk, dv); checked against central differences of the (separately pinned) forward.
+
+def _loss(fwd, q, k, v, do, scale, causal, lens, window):
+    o, _ = fwd(q, k, v, scale, causal, lens, window=window)
+    return float(np.sum(o * do))
+
+
+def _fd_grad(fwd, x, which, args, h=1e-6):
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        idx = it.multi_index
+        xp = x.copy(); xp[idx] += h
+        xm = x.copy(); xm[idx] -= h
+        g[idx] = (_loss(fwd, *args(which, xp)) - _loss(fwd, *args(which, xm))) / (2 * h)
+    return g
+
+
+def pin_bwd_finite_differences(impl, fwd):
+    cases = [
+        # (B, H, Nq, Nk, d, causal, lens, window, seed)
+        (1, 1, 4, 4, 3, False, None, None, 31),
+        (1, 2, 5, 5, 2, True, None, None, 32),
+        (2, 1, 3, 6, 3, False, [6, 2], None, 33),
+        (1, 1, 6, 6, 2, False, None, (1, 1), 34),
+        (2, 1, 4, 4, 2, True, [4, 3], None, 35),
+    ]
+    for bsz, heads, nq, nk, d, causal, lens, window, seed in cases:
+        r = _rng(seed)
+        q = r.standard_normal((bsz, heads, nq, d))
+        k = r.standard_normal((bsz, heads, nk, d))
+        v = r.standard_normal((bsz, heads, nk, d + 1))
+        do = r.standard_normal((bsz, heads, nq, d + 1))
+        scale = 0.8
+        dq, dk, dv = impl(q, k, v, do, scale, causal, lens, window=window)
+
+        def args(which, x):
+            qq, kk, vv = (x if which == 0 else q), (x if which == 1 else k), (x if which == 2 else v)
+            return qq, kk, vv, do, scale, causal, lens, window
+        for which, (g, x) in enumerate(((dq, q), (dk, k), (dv, v))):
+            _close(g, _fd_grad(fwd, x, which, args), 1e-7, f"grad {'qkv'[which]} vs central differences seed={seed}")
+
+
+def pin_bwd_single_key(impl, fwd):
+    # One allowed key: the softmax is constant 1, so dQ = dK = 0 and dV_0 = sum_i dO_i.
+    r = _rng(36)
+    q = r.standard_normal((2, 2, 4, 3))
+    k = r.standard_normal((2, 2, 5, 3))
+    v = r.standard_normal((2, 2, 5, 3))
+    do = r.standard_normal((2, 2, 4, 3))
+    dq, dk, dv = impl(q, k, v, do, 0.7, False, [1, 1])
+    assert np.all(dq == 0.0) and np.all(dk == 0.0), "single key: dQ = dK = 0"
+    _close(dv[:, :, 0], do.sum(axis=2), 1e-14, "single key: dV_0 = sum dO")
+    assert np.all(dv[:, :, 1:] == 0.0), "keys past the length get no gradient"
+
+
+def pin_bwd_uniform(impl, fwd):
+    # Q = 0: uniform weights over the allowed keys, so dV_j = sum_{i: j in A_i} dO_i / |A_i|.
+    r = _rng(37)
+    q = np.zeros((1, 2, 6, 3))
+    k = r.standard_normal((1, 2, 6, 3))
+    v = r.standard_normal((1, 2, 6, 2))
+    do = r.standard_normal((1, 2, 6, 2))
+    _, _, dv = impl(q, k, v, do, 0.9, True, None)
+    ref = np.zeros_like(dv)
+    for i in range(6):
+        ref[:, :, : i + 1] += do[:, :, i : i + 1] / (i + 1)
+    _close(dv, ref, 1e-14, "Q=0 causal dV")
+
+
+def pin_bwd_key_shift_sums(impl, fwd):
+    # O does not change when every key moves by the same vector t, so the derivative of the loss
+    # along that move, sum_j dK_j . t, is 0 for every t: sum_j dK_j = 0 per (b, h).
+    r = _rng(38)
+    q = r.standard_normal((2, 2, 5, 4))
+    k = r.standard_normal((2, 2, 5, 4))
+    v = r.standard_normal((2, 2, 5, 3))
+    do = r.standard_normal((2, 2, 5, 3))
+    for causal, lens in ((False, [5, 3]), (True, None)):
+        _, dk, _ = impl(q, k, v, do, 0.6, causal, lens)
+        _close(dk.sum(axis=2), np.zeros((2, 2, 4)), 1e-13, "sum_j dK_j = 0")
+
+
+BWD_PINS = [pin_bwd_finite_differences, pin_bwd_single_key, pin_bwd_uniform, pin_bwd_key_shift_sums]

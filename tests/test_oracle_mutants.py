@@ -151,3 +151,58 @@ def test_unmutated_window_copy_passes_every_pin():
     impl = make_window_mutant("none")
     for pin in WINDOW_PINS:
         pin(impl)
+
+
+# ---- planted mistakes in the backward pass, each of which must fail a backward pin
+from oracle import attention_fwd  # noqa: E402
+from oracle_pins import BWD_PINS  # noqa: E402
+
+
+def _fwd(q, k, v, scale, causal=False, kv_seqlens=None, return_p=False, window=None):
+    return attention_fwd(q, k, v, scale, causal=causal, kv_seqlens=kv_seqlens, return_p=return_p,
+                         window=window)
+
+
+def make_bwd_mutant(kind):
+    def impl(q, k, v, do, scale, causal=False, kv_seqlens=None, window=None):
+        bsz, heads, nq, _ = q.shape
+        dq = np.zeros_like(q); dk = np.zeros_like(k); dv = np.zeros_like(v)
+        _, _, p_all = _fwd(q, k, v, scale, causal, kv_seqlens, return_p=True, window=window)
+        for b in range(bsz):
+            for h in range(heads):
+                p = p_all[b, h]
+                dv[b, h] = (p @ do[b, h][: p.shape[1]] if kind == "dv_not_transposed" and p.shape[0] == p.shape[1]
+                            else p.T @ do[b, h])
+                dp = do[b, h] @ v[b, h].T
+                d_i = np.sum(p * dp, axis=1)
+                ds = p * dp if kind == "no_row_term" else p * (dp - d_i[:, None])
+                sq = 1.0 if kind == "dq_no_scale" else scale
+                dq[b, h] = sq * (ds @ k[b, h])
+                dk[b, h] = scale * (ds @ q[b, h] if kind == "dk_not_transposed" and ds.shape[0] == ds.shape[1]
+                                    else ds.T @ q[b, h])
+                if kind == "dk_sign":
+                    dk[b, h] = -dk[b, h]
+        return dq, dk, dv
+    return impl
+
+
+BWD_MUTANTS = ["dv_not_transposed", "no_row_term", "dq_no_scale", "dk_not_transposed", "dk_sign"]
+
+
+@pytest.mark.parametrize("kind", BWD_MUTANTS)
+def test_backward_mutant_fails_some_pin(kind):
+    impl = make_bwd_mutant(kind)
+    failed = []
+    for pin in BWD_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(impl, _fwd)
+        except (AssertionError, FloatingPointError, ValueError, OverflowError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {kind} passed every backward pin"
+
+
+def test_unmutated_backward_copy_passes_every_pin():
+    impl = make_bwd_mutant("none")
+    for pin in BWD_PINS:
+        pin(impl, _fwd)

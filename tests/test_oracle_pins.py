@@ -3,9 +3,9 @@
 import numpy as np
 import pytest
 
-from oracle import attention_fwd, bf16_bits_to_f64
+from oracle import attention_bwd, attention_fwd, bf16_bits_to_f64
 
-from oracle_pins import ALL_PINS, WINDOW_PINS
+from oracle_pins import ALL_PINS, BWD_PINS, WINDOW_PINS
 
 
 def oracle_impl(q, k, v, scale, causal=False, kv_seqlens=None, return_p=False, window=None):
@@ -16,6 +16,15 @@ def oracle_impl(q, k, v, scale, causal=False, kv_seqlens=None, return_p=False, w
 @pytest.mark.parametrize("pin", ALL_PINS + WINDOW_PINS, ids=lambda f: f.__name__)
 def test_oracle_pin(pin):
     pin(oracle_impl)
+
+
+def oracle_bwd(q, k, v, do, scale, causal=False, kv_seqlens=None, window=None):
+    return attention_bwd(q, k, v, do, scale, causal=causal, kv_seqlens=kv_seqlens, window=window)
+
+
+@pytest.mark.parametrize("pin", BWD_PINS, ids=lambda f: f.__name__)
+def test_oracle_backward_pin(pin):
+    pin(oracle_bwd, oracle_impl)
 
 
 def test_rows_subset_equals_full():
