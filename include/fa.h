@@ -104,6 +104,24 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
                   const int32_t* cu_seqlens_k, void* stream);
 
 /*
+ * fa_bwd -- backward pass of fa_fwd: the gradients dq, dk, dv of O for an upstream gradient
+ * dout, recomputing S and P tile by tile from q, k and the forward's lse instead of storing P
+ * (training needs this recomputation: page "FlashAttention：把注意力从公式写成数据流", section
+ * "用实验验证而不是背诵结论"; page "[2205.14135] FlashAttention ...", section "三、FLOPs"). With
+ * D_i = dout_i . o_i, per allowed pair (i, j): P_ij = exp(scale q_i.k_j - lse_i),
+ * dv_j += P_ij dout_i, dS_ij = P_ij (dout_i . v_j - D_i), dq_i += scale dS_ij k_j,
+ * dk_j += scale dS_ij q_i. Keys at or past L_b get dk = dv = 0; rows without keys get dq = 0.
+ *   q, k, v, o, dout, dq, dk, dv: bf16 in the fa_fwd layouts ([B][H][Nq or Nk][d]); lse: the fp32
+ *   [B][H][Nq] fa_fwd wrote for the same inputs, scale, mask and lengths. Arguments as for fa_fwd
+ *   (any Nq). bf16 products on the matrix cores with fp32 accumulation; P and dS rounded to bf16
+ *   before their products; gradients rounded to bf16 once. Deterministic (no atomics). A
+ *   workspace of 4*B*H*Nq bytes is allocated and freed stream-ordered on `stream`.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d,
+           float scale, int causal, const int32_t* kv_seqlens, void* stream);
+
+/*
  * fa_std_fwd -- the same bf16 operation computed by the standard, materialising algorithm, the
  * baseline the tiled path is measured against (page "FlashAttention：把注意力从公式写成数据流",
  * opening paragraph: S = Q K^T is written to device memory, read back for the softmax, and P is

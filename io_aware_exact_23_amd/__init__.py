@@ -13,6 +13,8 @@ Entry points mirror the C ABI in ``include/fa.h``:
   kv_seqlens, stream)`` -- bf16, sliding-window mask
 * ``fa_fwd_varlen(q, k, v, o, lse, B, H, total_q, total_k, max_seqlen_q, d, scale, window_left,
   window_right, cu_seqlens_q, cu_seqlens_k, stream)`` -- bf16, packed variable-length batch
+* ``fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, kv_seqlens,
+  stream)`` -- bf16 backward pass (gradients of fa_fwd)
 * ``fa_std_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, workspace,
   workspace_bytes, stream)`` -- bf16, standard (materialising) algorithm, the baseline
 * ``fa_std_workspace_bytes(B, H, Nq, Nk)``
@@ -34,7 +36,8 @@ import math
 import os
 from typing import Optional, Tuple
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_window", "fa_fwd_varlen", "fa_std_fwd",
+__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_window", "fa_fwd_varlen", "fa_bwd",
+           "attention_backward", "fa_std_fwd",
            "fa_std_workspace_bytes", "fa_status_string", "fa_last_error", "attention",
            "varlen_attention", "standard_attention", "library_path", "load_library"]
 
@@ -78,6 +81,8 @@ def load_library():
     lib.fa_fwd_window.restype = ci
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, vp, vp, vp]
     lib.fa_fwd_varlen.restype = ci
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp, vp]
+    lib.fa_bwd.restype = ci
     lib.fa_std_fwd.argtypes = sig[:13] + [vp, ctypes.c_size_t, vp]
     lib.fa_std_fwd.restype = ci
     lib.fa_std_workspace_bytes.argtypes = [ci, ci, ci, ci]
@@ -156,6 +161,33 @@ def fa_fwd_varlen(q, k, v, o, lse, B, H, total_q, total_k, max_seqlen_q, d, scal
                              int(total_q), int(total_k), int(max_seqlen_q), int(d), float(scale),
                              int(window_left), int(window_right), _ptr(cu_seqlens_q),
                              _ptr(cu_seqlens_k), _stream(stream)))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, kv_seqlens=None,
+           stream=None) -> None:
+    """bf16 backward pass; see include/fa.h for the contract."""
+    lib = load_library()
+    _raise(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                      _ptr(dv), int(B), int(H), int(Nq), int(Nk), int(d), float(scale), int(causal),
+                      _ptr(kv_seqlens), _stream(stream)))
+
+
+def attention_backward(q, k, v, o, lse, dout, scale: Optional[float] = None, causal: bool = False,
+                       kv_seqlens=None, stream=None):
+    """dQ, dK, dV (bf16) of attention(q, k, v) for the upstream gradient dout, given the forward's
+    o and lse."""
+    import torch
+
+    B, H, Nq, Nk, d = _check_qkv(q, k, v, kv_seqlens, (torch.bfloat16,))
+    for t in (o, dout):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (B, H, Nq, d) or not t.is_contiguous():
+            raise ValueError("o and dout must be contiguous bf16 [B, H, Nq, d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, d, scale, int(bool(causal)), kv_seqlens,
+           stream)
+    return dq, dk, dv
 
 
 def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,

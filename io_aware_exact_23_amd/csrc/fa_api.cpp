@@ -16,6 +16,7 @@ hipError_t launch_prefill_bf16_general(const PrefillParams& p, int d, int max_nq
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_standard(const StandardParams& p, int d, hipStream_t stream);
+hipError_t launch_backward(const BackwardParams& p, int d, hipStream_t stream);
 int prefill_bf16_rows_per_wg(int d);
 int prefill_bf16_pp_rows_per_wg();
 constexpr int kPrefillLongNq = 2048;  // query rows from which the 8-wave prefill kernel is used
@@ -151,6 +152,71 @@ extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float*
   fa::PrefillParams p = prefill_params(q, k, v, o, lse, B, H, Nq, Nk, scale, causal, kv_seqlens);
   hipError_t e = fa::launch_prefill_f32(p, d, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail_hip(e, "prefill launch");
+  return FA_OK;
+}
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+                      int d, float scale, int causal, const int32_t* kv_seqlens, void* stream) {
+  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens);
+  if (st == 1) {
+    // No query rows: dK and dV are still defined, zero, when there are keys (the dK/dV kernel
+    // writes them without visiting any query tile; the other kernels have no rows to run on).
+    if ((int64_t)B * H > 0 && Nk > 0 && Nq == 0) {
+      if (!dk || !dv) return fail(FA_ERR_INVALID_ARGUMENT, "dk and dv must be non-null");
+      if (!aligned(dk, 16) || !aligned(dv, 16))
+        return fail(FA_ERR_INVALID_ARGUMENT, "dout, dq, dk and dv must be 16-byte aligned");
+      fa::BackwardParams p{};
+      p.dk = dk;
+      p.dv = dv;
+      p.k = k;
+      p.v = v;
+      p.kv_seqlens = kv_seqlens;
+      p.B = B;
+      p.H = H;
+      p.Nk = Nk;
+      p.scale = scale;
+      hipError_t e = fa::launch_backward(p, d, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return fail_hip(e, "backward launch");
+    }
+    return FA_OK;
+  }
+  if (st != FA_OK) return st;
+  if (!dout || !dq || (Nk > 0 && (!dk || !dv)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "dout, dq, dk and dv must be non-null");
+  if (!aligned(dout, 16) || !aligned(dq, 16) || (dk && !aligned(dk, 16)) || (dv && !aligned(dv, 16)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "dout, dq, dk and dv must be 16-byte aligned");
+  const int64_t bh = (int64_t)B * H;
+  if (bh * ((Nq + 127) / 128) > std::numeric_limits<int32_t>::max() ||
+      bh * ((Nk + 127) / 128) > std::numeric_limits<int32_t>::max() ||
+      (bh * Nq + 3) / 4 > std::numeric_limits<int32_t>::max())
+    return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  fa::BackwardParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.kv_seqlens = kv_seqlens;
+  p.B = B;
+  p.H = H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.scale = scale;
+  p.causal = causal;
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, (size_t)bh * Nq * sizeof(float), s);
+  if (e != hipSuccess) return fail_hip(e, "hipMallocAsync(backward workspace)");
+  p.delta = static_cast<float*>(ws);
+  e = fa::launch_backward(p, d, s);
+  hipError_t ef = hipFreeAsync(ws, s);
+  if (e == hipSuccess) e = ef;
+  if (e != hipSuccess) return fail_hip(e, "backward launch");
   return FA_OK;
 }
 

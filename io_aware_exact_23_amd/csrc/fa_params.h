@@ -40,6 +40,24 @@ struct DecodeParams {
   float c;            // scale * log2(e)
 };
 
+// Backward pass: gradients of the forward for an upstream gradient dO (all bf16 but lse).
+struct BackwardParams {
+  const void* q;     // [B][H][Nq][D]
+  const void* k;     // [B][H][Nk][D]
+  const void* v;     // [B][H][Nk][D]
+  const void* o;     // [B][H][Nq][D] forward output
+  const void* dout;  // [B][H][Nq][D] upstream gradient
+  const float* lse;  // [B][H][Nq] forward logsumexp (natural log)
+  void* dq;          // [B][H][Nq][D]
+  void* dk;          // [B][H][Nk][D]
+  void* dv;          // [B][H][Nk][D]
+  const int32_t* kv_seqlens;
+  float* delta;      // [B][H][Nq] workspace: D_i = dO_i . O_i
+  int B, H, Nq, Nk;
+  float scale;
+  int causal;
+};
+
 // Standard (materialising) attention: S = scale * Q K^T and P = softmax(S) both go to device
 // memory, then O = P V. Rows of S and P are ld elements apart (ld = Nk rounded up to 64).
 struct StandardParams {

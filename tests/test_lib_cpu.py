@@ -23,7 +23,7 @@ def declared_functions():
 
 
 def test_header_declares_the_abi():
-    assert declared_functions() == ["fa_fwd", "fa_fwd_f32", "fa_fwd_varlen", "fa_fwd_window",
+    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_f32", "fa_fwd_varlen", "fa_fwd_window",
                                     "fa_last_error", "fa_status_string", "fa_std_fwd",
                                     "fa_std_workspace_bytes"]
 
@@ -200,4 +200,39 @@ def test_varlen_empty_is_a_no_op(args):
     call = dict(VARLEN)
     call.update(args)
     fa.fa_fwd_varlen(**call)
+    assert fa.fa_last_error() == ""
+
+
+BWD = dict(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, dk=A, dv=A, B=2, H=3, Nq=8, Nk=8, d=64,
+           scale=0.125, causal=0, kv_seqlens=None, stream=0)
+
+
+@needs_lib
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED, "64 or 128"),
+    (dict(Nk=-1), fa.FA_ERR_INVALID_ARGUMENT, ">= 0"),
+    (dict(causal=1, Nq=4, Nk=5), fa.FA_ERR_UNSUPPORTED, "Nq == Nk"),
+    (dict(dout=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(dq=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(dk=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(dv=A + 4), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(dout=A + 8), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARGUMENT, "finite"),
+    (dict(Nq=0, dk=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+])
+def test_backward_argument_errors(args, status, needle):
+    call = dict(BWD)
+    call.update(args)
+    with pytest.raises(fa.FaError) as ei:
+        fa.fa_bwd(**call)
+    assert ei.value.status == status
+    assert needle in ei.value.message
+
+
+@needs_lib
+@pytest.mark.parametrize("args", [dict(B=0), dict(H=0), dict(Nq=0, Nk=0)])
+def test_backward_empty_is_a_no_op(args):
+    call = dict(BWD)
+    call.update(args)
+    fa.fa_bwd(**call)
     assert fa.fa_last_error() == ""
