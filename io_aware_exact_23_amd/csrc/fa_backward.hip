@@ -377,15 +377,17 @@ void bwd_dkdv_kernel(BackwardParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) dk[db][e] = dv[db][e] = 0.0f;
 
+  // One 32-query block at a time: S and dP of the block, then its P and dS, then its two 16-query
+  // steps of dV^T and dK^T (keeps the live accumulators to those of one block).
   auto step = [&](const char* stage, int qt0) {
     const char* Qs = stage;
     const char* dOs = stage + C::kTileBytes;
     const float* ls = reinterpret_cast<const float*>(stage + 2 * C::kTileBytes);
-    f32x16 s[2], dp[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+      f32x16 s, dp;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[qb][e] = dp[qb][e] = 0.0f;
+      for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
       const char* qrow = Qs + (qb * 32 + qr) * C::kRowBytes;
       const char* drow = dOs + (qb * 32 + qr) * C::kRowBytes;
 #pragma unroll
@@ -393,14 +395,11 @@ void bwd_dkdv_kernel(BackwardParams p) {
         const int pc = ((2 * ks + g) ^ qsw) << 4;
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qrow + pc);
         const bf16x8 da = *reinterpret_cast<const bf16x8*>(drow + pc);
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], s[qb], 0, 0, 0);
-        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[ks], dp[qb], 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[ks], dp, 0, 0, 0);
       }
-    }
-    // Entry e of block qb is query qt0 + qb*32 + 16(e/8) + 8g + e%8 against this lane's key kj.
-    bf16x8 pb[2][2], dsb[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      // Entry e is query qt0 + qb*32 + 16(e/8) + 8g + e%8 against this lane's key kj.
+      bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int ql = qb * 32 + 16 * hh + 8 * g;  // tile-local query of entry hh*8
@@ -420,28 +419,27 @@ void bwd_dkdv_kernel(BackwardParams p) {
             const float lq = j < 4 ? l0[j] : l1[j - 4];
             const float dq = j < 4 ? d0[j] : d1[j - 4];
             const bool ok = kj < L && (!p.causal || kj <= qq);
-            pv[u] = ok ? fast_exp2(fmaf(s[qb][e], c, -lq)) : 0.0f;
-            dsv[u] = pv[u] * (dp[qb][e] - dq);
+            pv[u] = ok ? fast_exp2(fmaf(s[e], c, -lq)) : 0.0f;
+            dsv[u] = pv[u] * (dp[e] - dq);
           }
           xp[t] = pack_bf16(pv[0], pv[1]);
           xs[t] = pack_bf16(dsv[0], dsv[1]);
         }
-        pb[qb][hh] = __builtin_bit_cast(bf16x8, xp);
-        dsb[qb][hh] = __builtin_bit_cast(bf16x8, xs);
+        pb[hh] = __builtin_bit_cast(bf16x8, xp);
+        dsb[hh] = __builtin_bit_cast(bf16x8, xs);
       }
-    // dV^T += dO^T P and dK^T += Q^T dS over the tile's four 16-query steps.
+      // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-query steps.
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int o = u * 16 * C::kRowBytes + tr_off[db];
-        const s16x4 da8[2] = {lds_read_tr16(dOs + o), lds_read_tr16(dOs + o + 4 * C::kRowBytes)};
-        const s16x4 qa8[2] = {lds_read_tr16(Qs + o), lds_read_tr16(Qs + o + 4 * C::kRowBytes)};
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, da8), pb[u >> 1][u & 1],
-                                                        dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa8), dsb[u >> 1][u & 1],
-                                                        dk[db], 0, 0, 0);
-      }
+        for (int db = 0; db < D / 32; ++db) {
+          const int o = (qb * 2 + hh) * 16 * C::kRowBytes + tr_off[db];
+          const s16x4 da8[2] = {lds_read_tr16(dOs + o), lds_read_tr16(dOs + o + 4 * C::kRowBytes)};
+          const s16x4 qa8[2] = {lds_read_tr16(Qs + o), lds_read_tr16(Qs + o + 4 * C::kRowBytes)};
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, da8), pb[hh], dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa8), dsb[hh], dk[db], 0, 0, 0);
+        }
+    }
   };
 
   if (t0 < tn) {
