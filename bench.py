@@ -7,14 +7,17 @@ decode workload (B=64, H=32, Nk=8192 cache with valid lengths in [1024, 8192], d
 the same run and reported under "decode". Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode]
-                  [--no-standard] [--no-cpu-baseline] [--cpu-seconds S] [--calibrate-copy]
+                  [--no-standard] [--no-masks] [--no-backward] [--no-cpu-baseline]
+                  [--cpu-seconds S] [--calibrate-copy]
 
 The standard (materialising) algorithm, fa_std_fwd, is timed on the three prefill workloads and
 reported under "standard_attention" with its speedup ratio against fa_fwd (the pages' headline
 comparison) and the HBM roofline of the whole call on the default workload. The generalised masks
 are timed on the long workload's shape and reported under "masks": a causal sliding window of
 4096 keys (fa_fwd_window) and the same batch packed as variable-length sequences
-(fa_fwd_varlen), with FLOPs counted over the allowed (query, key) pairs.
+(fa_fwd_varlen), with FLOPs counted over the allowed (query, key) pairs. The backward pass,
+fa_bwd, is timed on the 16K causal and GPT-2 shapes and reported under "backward", its FLOPs
+counted as the five products of the gradient.
 
 FLOPs are counted as 4*B*H*Nq*Nk*d, halved for causal masking. Decode bytes are the algorithmic
 HBM bytes: Q, the valid K and V rows, O and lse.
@@ -237,6 +240,44 @@ def bench_masks(fa, configs, inputs, torch, dev, steps, warmup):
     return out
 
 
+def bench_backward(fa, configs, inputs, torch, dev, steps, warmup):
+    """fa_bwd (dQ, dK, dV from the saved lse) on the 16K causal and GPT-2 shapes.
+
+    FLOPs are counted as the five matrix products of the gradient (S, dP, dV, dK, dQ), 2.5 times
+    the forward count; the kernels compute seven (the dQ kernel recomputes S and dP).
+    """
+    out = {"unit": "TFLOP/s", "peak": PEAK_MFMA_BF16_TFLOPS, "counted_products": 5, "workloads": []}
+    for name in ["long_causal_b2_h16_n16384_d128", "gpt2s_causal_b8_h12_n1024_d64"]:
+        w = configs.BY_NAME[name]
+        q, k, v, lens = inputs.make(w, dev)
+        do = inputs.normal((w.B, w.H, w.Nq, w.d), w.seed + 7, dev, "bf16", 1.0)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+        fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal), lens, None)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+        def bstep():
+            fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal),
+                      lens, None)
+
+        n = steps if w.Nq <= LONG_NQ else max(3, steps // 4)
+        t, per = time_launches(bstep, n, warmup, torch)
+        avg = float(np.mean(per))
+        fl = int(2.5 * w.counted_flops())
+        rec = {"workload": name, "ms_per_step": round(t / n * 1e3, 4), "counted_flops": fl,
+               "value": round(fl * n / t / 1e12, 2)}
+        if name == configs.LONG_CAUSAL_16K.name:
+            rec["roofline"] = {"kernel": "bwd_delta_kernel + bwd_dq_kernel + bwd_dkdv_kernel (whole call)",
+                               "bound": "mfma", "achieved": round(fl / avg / 1e12, 2),
+                               "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(fl / avg / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
+                               "avg_launch_ms": round(avg * 1e3, 4)}
+        out["workloads"].append(rec)
+        del q, k, v, do, o, dq, dk, dv
+        torch.cuda.empty_cache()
+    return out
+
+
 def decode_bytes(w, lens) -> int:
     per_key = 2 * w.d * 2                      # one K row and one V row, bf16
     per_bh = 2 * w.d * 2 + 4                   # Q and O rows (bf16) and lse (fp32)
@@ -254,6 +295,8 @@ def main():
                     help="skip the standard-algorithm comparison (fa_std_fwd)")
     ap.add_argument("--no-masks", action="store_true",
                     help="skip the sliding-window and packed-sequence timings")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass timing (fa_bwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -348,6 +391,9 @@ def main():
 
     if not args.no_masks:
         result["masks"] = bench_masks(fa, configs, inputs, torch, dev, args.steps, args.warmup)
+
+    if not args.no_backward:
+        result["backward"] = bench_backward(fa, configs, inputs, torch, dev, args.steps, args.warmup)
 
     if not args.no_standard and w.Nq > 1 and w.dtype == "bf16":
         result["standard_attention"] = bench_standard(fa, configs, inputs, torch, dev, args.steps,
