@@ -416,3 +416,192 @@ def pin_bwd_key_shift_sums(impl, fwd):
 
 
 BWD_PINS = [pin_bwd_finite_differences, pin_bwd_single_key, pin_bwd_uniform, pin_bwd_key_shift_sums]
+
+
+# ---- FP8 (e4m3) path. Each pin takes a namespace ``f`` with the oracle's functions: decode,
+# round, quantize, attention (attention_fwd_fp8) and bound (p_rounding_bound), and pins them to
+# torch's own float8_e4m3fn conversion (a library routine of the same format), exact rational
+# arithmetic, 50-digit brute force, and a simulation of the probability rounding.
+
+def _torch_e4m3_codes(x):
+    import torch
+    t = torch.tensor(np.asarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _torch_e4m3_values(codes):
+    import torch
+    t = torch.tensor(np.asarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _finite_positive_table():
+    codes = np.arange(0x7F, dtype=np.uint8)  # 0x00 .. 0x7E: +0 and every positive finite value
+    return codes, _torch_e4m3_values(codes)
+
+
+def pin_fp8_decode_table(f):
+    codes = np.arange(256, dtype=np.uint8)
+    got = np.asarray(f.decode(codes), dtype=np.float64)
+    ref = _torch_e4m3_values(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), "NaN codes"
+    assert np.array_equal(got[~nan], ref[~nan]), "decoded values differ from the library's"
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan])), "signs"
+    # Landmarks of the format: largest finite, smallest normal, smallest subnormal, one.
+    assert got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9 and got[0x38] == 1.0
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and got[0xFE] == -448.0
+
+
+def pin_fp8_round_library(f):
+    rng = _rng(101)
+    mags = np.exp2(rng.uniform(-13.0, np.log2(460.0), 4000))
+    _, vals = _finite_positive_table()
+    mids = (vals[:-1] + vals[1:]) / 2.0          # every tie between neighbours below 448
+    x = np.concatenate([mags, vals, mids, mids * (1 + 2.0 ** -20), mids * (1 - 2.0 ** -20), [0.0]])
+    x = np.concatenate([x, -x]).astype(np.float32).astype(np.float64)
+    got = np.asarray(f.round(x))
+    ref = _torch_e4m3_codes(x)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, f"codes differ from the library's at x = {x[bad[:5]]}"
+
+
+def pin_fp8_round_nearest(f):
+    codes, vals = _finite_positive_table()
+    rng = _rng(102)
+    x = np.concatenate([np.exp2(rng.uniform(-12.0, 8.8, 3000)), (vals[1:] + vals[:-1]) / 2.0])
+    x = x[x <= 448.0]
+    got = np.asarray(f.round(x)).astype(np.int64)
+    for xi, c in zip(x, got):
+        dist = np.abs(vals - xi)
+        best = np.nonzero(dist == dist.min())[0]
+        assert c in codes[best], f"{xi}: code {c:#x} is not a nearest value"
+        if best.size > 1:
+            assert c % 2 == 0, f"{xi}: tie not resolved to the even mantissa"
+
+
+def pin_fp8_round_trip_and_saturation(f):
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    back = np.asarray(f.round(np.asarray(f.decode(codes), dtype=np.float64)))
+    assert np.array_equal(back, codes), "encode(decode(c)) != c"
+    sat = np.asarray(f.round(np.array([448.0, 470.0, 1.0e6, -500.0, np.inf])))
+    assert list(sat) == [0x7E, 0x7E, 0x7E, 0xFE, 0x7E], f"saturation: {sat}"
+    assert int(np.asarray(f.round(np.array([np.nan])))[0]) & 0x7F == 0x7F
+
+
+def _fp32_nearest(fr):
+    """The fp32 value nearest to the Fraction fr (ties to even), found with exact arithmetic."""
+    from fractions import Fraction
+    c = np.float32(float(fr))
+    best = None
+    for cand in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        dist = abs(Fraction(float(cand)) - fr)
+        key = (dist, int(np.frombuffer(np.float32(cand).tobytes(), dtype=np.uint32)[0]) & 1)
+        if best is None or key < best[0]:
+            best = (key, cand)
+    return np.float32(best[1])
+
+
+def _bf16_grid(shape, seed, std=1.0):
+    x = _rng(seed).normal(0.0, std, shape).astype(np.float32)
+    b = (x.view(np.uint32) + np.uint32(0x8000)) & np.uint32(0xFFFF0000)  # round to bf16
+    return b.view(np.float32).astype(np.float64)
+
+
+def pin_fp8_quantize(f):
+    from fractions import Fraction
+    B, H, N, d = 2, 3, 70, 16
+    x = _bf16_grid((B, H, N, d), 103, 2.0)
+    x[1, 2] = 0.0                                   # an all-zero slice
+    lens = [70, 33]
+    poisoned = x.copy()
+    poisoned[1, :, 33:] = 1.0e4
+    codes, s = f.quantize(poisoned, kv_seqlens=lens)
+    codes = np.asarray(codes)
+    s = np.asarray(s, dtype=np.float32)
+    codes0, s0 = f.quantize(x, kv_seqlens=lens)
+    assert np.array_equal(codes, np.asarray(codes0)) and np.array_equal(s, np.asarray(s0)), \
+        "rows past the length changed the result"
+    assert np.all(codes[1, :, 33:] == 0), "rows past the length must be stored as zero"
+    assert s[1, 2] == 1.0 and np.all(codes[1, 2] == 0), "all-zero slice"
+    for b in range(B):
+        L = lens[b]
+        for h in range(H):
+            rows = x[b, h, :L]
+            amax = np.max(np.abs(rows))
+            if amax == 0:
+                continue
+            # s is the fp32 value nearest to amax / 448 (exact rational arithmetic).
+            assert s[b, h] == _fp32_nearest(Fraction(float(amax)) / 448), f"scale of ({b}, {h})"
+            # Codes: e4m3 of the fp32 quotient x / s, the quotient rounded with exact arithmetic.
+            sf = Fraction(float(s[b, h]))
+            y = np.array([_fp32_nearest(Fraction(float(v)) / sf) for v in rows.ravel()],
+                         dtype=np.float32)
+            want = _torch_e4m3_codes(y).reshape(rows.shape)
+            assert np.array_equal(codes[b, h, :L], want), f"codes of ({b}, {h})"
+            # The largest magnitude maps to +-448; dequantised values are within half a unit.
+            at = np.abs(rows) == amax
+            assert np.all(np.isin(codes[b, h, :L][at], [0x7E, 0xFE]))
+            deq = np.asarray(f.decode(codes[b, h, :L])) * float(s[b, h])
+            assert np.all(np.abs(deq - rows) <= 2.0 ** -4 * np.abs(rows) + 2.0 ** -10 * float(s[b, h]) * 1.001)
+    # Transposed layout: V^T per (b, h), columns padded with zeros to a multiple of 64.
+    ct, st = f.quantize(poisoned, kv_seqlens=lens, transpose=True)
+    ct = np.asarray(ct)
+    assert ct.shape == (B, H, d, 128) and np.array_equal(np.asarray(st), s)
+    assert np.array_equal(ct[:, :, :, :N], np.swapaxes(codes, 2, 3)) and np.all(ct[:, :, :, N:] == 0)
+
+
+def pin_fp8_attention_brute_force(f):
+    # Small codes with non-power-of-two scales against the 50-digit definition of the dequantised
+    # values (V given transposed, as the path stores it).
+    B, H, Nq, Nk, d = 1, 2, 5, 7, 4
+    rng = _rng(104)
+    q8 = rng.integers(0, 256, (B, H, Nq, d)).astype(np.uint8)
+    k8 = rng.integers(0, 256, (B, H, Nk, d)).astype(np.uint8)
+    v8 = rng.integers(0, 256, (B, H, Nk, d)).astype(np.uint8)
+    for a in (q8, k8, v8):
+        a[(a & 0x7F) == 0x7F] = 0x30  # no NaN codes
+        a[(a & 0x7F) > 0x50] &= 0xC7  # keep magnitudes moderate
+    dq = np.array([[0.37, 1.9]], dtype=np.float32)
+    dk = np.array([[0.11, 0.6]], dtype=np.float32)
+    dv = np.array([[3.3, 0.07]], dtype=np.float32)
+    v8t = np.zeros((B, H, d, 64), dtype=np.uint8)
+    v8t[:, :, :, :Nk] = np.swapaxes(v8, 2, 3)
+    for causal, lens in ((False, None), (False, [4])):
+        o, lse = f.attention(q8, k8, v8t, dq, dk, dv, 0.5, causal=causal, kv_seqlens=lens)
+        qv = _torch_e4m3_values(q8) * dq[:, :, None, None].astype(np.float64)
+        kv = _torch_e4m3_values(k8) * dk[:, :, None, None].astype(np.float64)
+        vv = _torch_e4m3_values(v8) * dv[:, :, None, None].astype(np.float64)
+        o_ref, lse_ref = brute_force_mp(qv, kv, vv, 0.5, causal, lens)
+        _close(o, o_ref, 1e-12, "fp8 O vs brute force")
+        _close(lse, lse_ref, 1e-12, "fp8 lse vs brute force")
+
+
+def pin_fp8_bound_simulation(f):
+    # Round 8 * 2^(t - m') to e4m3 for offsets m' at or below the row maximum (the GPU path's
+    # lazy offset), normalise by the unrounded sum, and compare with the exact weights.
+    rng = _rng(105)
+    R, N = 256, 300
+    t = rng.uniform(-24.0, 0.0, (R, N))
+    t[rng.random((R, N)) < 0.1] = -np.inf                     # masked pairs
+    t[:, 0] = 0.0                                              # row maximum 0
+    p = np.exp2(t)
+    p = p / p.sum(axis=1, keepdims=True)
+    bound = np.asarray(f.bound(p))
+    worst = 0.0
+    for shift in (0.0, 0.7, 2.9):                              # m' = max - shift (p~ <= 2^shift)
+        pt = np.exp2(t + shift)
+        x = 8.0 * pt
+        qv = _torch_e4m3_values(_torch_e4m3_codes(x))
+        w = qv / (8.0 * pt.sum(axis=1, keepdims=True))
+        err = np.abs(w - p)
+        assert np.all(err <= bound * (1 + 1e-9) + 1e-300), "weight error above the bound"
+        ok = bound > 0
+        worst = max(worst, float(np.max(err[ok] / bound[ok])))
+    assert np.all(bound[np.isinf(t)] == 0.0), "masked pairs must get a zero bound"
+    assert worst > 0.5, f"bound far from tight ({worst:.3f}): it would hide real errors"
+
+
+FP8_PINS = [pin_fp8_decode_table, pin_fp8_round_library, pin_fp8_round_nearest,
+            pin_fp8_round_trip_and_saturation, pin_fp8_quantize, pin_fp8_attention_brute_force,
+            pin_fp8_bound_simulation]

@@ -206,3 +206,151 @@ def test_unmutated_backward_copy_passes_every_pin():
     impl = make_bwd_mutant("none")
     for pin in BWD_PINS:
         pin(impl, _fwd)
+
+
+# ---- FP8 (e4m3) oracle: planted mistakes in the format, the quantiser, the attention of the
+# quantised tensors and the rounding bound.
+
+from oracle import fp8 as _fp8  # noqa: E402
+from oracle_pins import FP8_PINS  # noqa: E402
+
+
+def _round_variant(x, bias=7, mode="even", sub_limit=2.0 ** -6, overflow="saturate"):
+    """A copy of the e4m3 rounding with switches for the planted mistakes."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    code = np.zeros(x.shape, dtype=np.int64)
+
+    def rnd(v):
+        if mode == "even":
+            return np.rint(v)
+        if mode == "half_up":
+            return np.floor(v + 0.5)
+        return np.floor(v)  # truncation
+
+    sub = a < sub_limit
+    code[sub] = rnd(a[sub] / 2.0 ** -9).astype(np.int64)
+    nrm = ~sub & np.isfinite(a)
+    f, e2 = np.frexp(a[nrm])
+    e = e2 - 1
+    m = rnd((2.0 * f - 1.0) * 8.0).astype(np.int64)
+    e = np.where(m == 8, e + 1, e)
+    m = np.where(m == 8, 0, m)
+    big = (e > 15 - bias) | ((e == 15 - bias) & (m == 7))
+    c = np.clip(e + bias, 0, 15) << 3 | m
+    code[nrm] = np.where(big, 0x7F if overflow == "nan" else 0x7E, c)
+    code[np.isinf(a)] = 0x7E
+    code |= np.where(np.signbit(x), 0x80, 0)
+    code[np.isnan(x)] = 0x7F
+    return code.astype(np.uint8)
+
+
+def _decode_bias8(codes):
+    c = np.asarray(codes).astype(np.int64)
+    v = _fp8.e4m3_decode(codes)
+    normal = ((c >> 3) & 0xF) != 0
+    return np.where(normal, v / 2.0, v)
+
+
+def _quantize_variant(kind):
+    def q(x, kv_seqlens=None, transpose=False):
+        x = np.asarray(x, dtype=np.float64)
+        bsz, heads, n, d = x.shape
+        codes = np.zeros((bsz, heads, n, d), dtype=np.uint8)
+        s_all = np.ones((bsz, heads), dtype=np.float32)
+        for b in range(bsz):
+            L = n if kv_seqlens is None else min(max(int(kv_seqlens[b]), 0), n)
+            Lq = n if kind in ("amax_all_rows", "padding_kept") else L
+            for h in range(heads):
+                rows = x[b, h, :Lq].astype(np.float32)
+                amax = np.float32(np.max(np.abs(x[b, h, :Lq if kind == "amax_all_rows" else L])))
+                top = np.float32(240.0 if kind == "scale_240" else 448.0)
+                s = np.float32(1.0) if amax == 0 else np.float32(amax / top)
+                s_all[b, h] = s
+                codes[b, h, :Lq] = _fp8.e4m3_round((rows / s).astype(np.float32).astype(np.float64))
+        if not transpose:
+            return codes, s_all
+        cols = n if kind == "transpose_no_pad" else _fp8.vt_cols(n)
+        out = np.zeros((bsz, heads, d, cols), dtype=np.uint8)
+        out[:, :, :, :n] = np.swapaxes(codes, 2, 3) if kind != "transpose_swapped_dims" else \
+            np.swapaxes(codes, 2, 3)[:, :, ::-1]
+        return out, s_all
+    return q
+
+
+def _attention_variant(kind):
+    def att(q8, k8, v8t, dq, dk, dv, scale, causal=False, kv_seqlens=None, rows=None, return_p=False):
+        nk = np.asarray(k8).shape[2]
+        q = _fp8.dequantize_e4m3(q8, dq)
+        k = _fp8.dequantize_e4m3(k8, dk if kind != "k_uses_q_scale" else dq)
+        v = _fp8.dequantize_e4m3(v8t, np.ones_like(dv) if kind == "no_dv" else dv, transposed=True, n=nk)
+        if kind == "v_not_transposed":
+            v = _fp8.dequantize_e4m3(np.asarray(v8t)[:, :, :nk, :], dv)
+        from oracle import attention_fwd
+        return attention_fwd(q, k, v, scale, causal=causal, kv_seqlens=kv_seqlens, rows=rows,
+                             return_p=return_p)
+    return att
+
+
+def _bound_variant(kind):
+    def bound(p):
+        p = np.asarray(p, dtype=np.float64)
+        inv_l = p.max(axis=-1, keepdims=True)
+        rel = 2.0 ** -5 if kind == "bound_half" else 2.0 ** -4
+        sub = 0.0 if kind == "bound_no_subnormal" else 2.0 ** -13
+        b = np.where(p > 0, rel * p + sub * inv_l, 0.0)
+        return 4.0 * b if kind == "bound_4x" else b
+    return bound
+
+
+def make_fp8_mutant(kind):
+    import types
+    ns = types.SimpleNamespace(decode=_fp8.e4m3_decode, round=_fp8.e4m3_round,
+                               quantize=_fp8.quantize_e4m3, attention=_fp8.attention_fwd_fp8,
+                               bound=_fp8.p_rounding_bound)
+    if kind == "decode_bias8":
+        ns.decode = _decode_bias8
+    elif kind == "round_bias8":
+        ns.round = lambda x: _round_variant(x, bias=8)
+    elif kind in ("round_half_up", "round_truncate"):
+        ns.round = lambda x: _round_variant(x, mode=kind[6:])
+    elif kind == "round_subnormal_limit":
+        ns.round = lambda x: _round_variant(x, sub_limit=2.0 ** -7)
+    elif kind == "round_nan_on_overflow":
+        ns.round = lambda x: _round_variant(x, overflow="nan")
+    elif kind == "round_copy_ok":
+        ns.round = lambda x: _round_variant(x)
+    elif kind in ("scale_240", "amax_all_rows", "padding_kept", "transpose_no_pad",
+                  "transpose_swapped_dims", "quantize_copy_ok"):
+        ns.quantize = _quantize_variant(kind)
+    elif kind in ("no_dv", "k_uses_q_scale", "v_not_transposed", "attention_copy_ok"):
+        ns.attention = _attention_variant(kind)
+    elif kind in ("bound_half", "bound_no_subnormal", "bound_4x", "bound_copy_ok"):
+        ns.bound = _bound_variant(kind)
+    return ns
+
+
+FP8_MUTANTS = ["decode_bias8", "round_bias8", "round_half_up", "round_truncate",
+               "round_subnormal_limit", "round_nan_on_overflow", "scale_240", "amax_all_rows",
+               "padding_kept", "transpose_no_pad", "transpose_swapped_dims", "no_dv",
+               "k_uses_q_scale", "v_not_transposed", "bound_half", "bound_no_subnormal", "bound_4x"]
+
+
+@pytest.mark.parametrize("kind", FP8_MUTANTS)
+def test_fp8_mutant_fails_some_pin(kind):
+    ns = make_fp8_mutant(kind)
+    failed = []
+    for pin in FP8_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(ns)
+        except (AssertionError, FloatingPointError, ValueError, OverflowError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {kind} passed every fp8 pin"
+
+
+@pytest.mark.parametrize("kind", ["round_copy_ok", "quantize_copy_ok", "attention_copy_ok", "bound_copy_ok"])
+def test_unmutated_fp8_copies_pass_every_pin(kind):
+    ns = make_fp8_mutant(kind)
+    for pin in FP8_PINS:
+        pin(ns)

@@ -5,7 +5,7 @@ import pytest
 
 from oracle import attention_bwd, attention_fwd, bf16_bits_to_f64
 
-from oracle_pins import ALL_PINS, BWD_PINS, WINDOW_PINS
+from oracle_pins import ALL_PINS, BWD_PINS, FP8_PINS, WINDOW_PINS
 
 
 def oracle_impl(q, k, v, scale, causal=False, kv_seqlens=None, return_p=False, window=None):
@@ -25,6 +25,20 @@ def oracle_bwd(q, k, v, do, scale, causal=False, kv_seqlens=None, window=None):
 @pytest.mark.parametrize("pin", BWD_PINS, ids=lambda f: f.__name__)
 def test_oracle_backward_pin(pin):
     pin(oracle_bwd, oracle_impl)
+
+
+def fp8_namespace():
+    import types
+
+    from oracle import fp8
+    return types.SimpleNamespace(decode=fp8.e4m3_decode, round=fp8.e4m3_round,
+                                 quantize=fp8.quantize_e4m3, attention=fp8.attention_fwd_fp8,
+                                 bound=fp8.p_rounding_bound)
+
+
+@pytest.mark.parametrize("pin", FP8_PINS, ids=lambda f: f.__name__)
+def test_oracle_fp8_pin(pin):
+    pin(fp8_namespace())
 
 
 def test_rows_subset_equals_full():
