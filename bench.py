@@ -7,7 +7,7 @@ decode workload (B=64, H=32, Nk=8192 cache with valid lengths in [1024, 8192], d
 the same run and reported under "decode". Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode]
-                  [--no-standard] [--no-masks] [--no-backward] [--no-cpu-baseline]
+                  [--no-standard] [--no-masks] [--no-backward] [--no-fp8] [--no-cpu-baseline]
                   [--cpu-seconds S] [--calibrate-copy]
 
 The standard (materialising) algorithm, fa_std_fwd, is timed on the three prefill workloads and
@@ -17,7 +17,9 @@ are timed on the long workload's shape and reported under "masks": a causal slid
 4096 keys (fa_fwd_window) and the same batch packed as variable-length sequences
 (fa_fwd_varlen), with FLOPs counted over the allowed (query, key) pairs. The backward pass,
 fa_bwd, is timed on the 16K causal and GPT-2 shapes and reported under "backward", its FLOPs
-counted as the five products of the gradient.
+counted as the five products of the gradient. The e4m3 path (fa_quantize_fp8 + fa_fwd_fp8) is
+timed on the 16K causal shape and reported under "fp8" with its roofline against the fp8 matrix
+peak, the conversion cost, and its output's distance from the bf16 path's.
 
 FLOPs are counted as 4*B*H*Nq*Nk*d, halved for causal masking. Decode bytes are the algorithmic
 HBM bytes: Q, the valid K and V rows, O and lse.
@@ -39,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (bf16) and % of MFMA peak; decode HBM GB/s"
 PEAK_MFMA_BF16_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_MFMA_FP8_TFLOPS = 5033.2    # MI355X dense fp8: 256 CU x 2.4 GHz x 8192 FLOP/clk
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 KERNEL_SOURCES = ["fa_prefill_bf16.hip", "fa_prefill_pp.hip", "fa_decode.hip", "fa_device.h", "fa_softmax.h",
                   "fa_params.h", "fa_api.cpp"]
@@ -278,6 +281,61 @@ def bench_backward(fa, configs, inputs, torch, dev, steps, warmup):
     return out
 
 
+def bench_fp8(fa, configs, inputs, torch, dev, steps, warmup):
+    """e4m3 forward on the 16K causal shape: conversion cost, forward rate, error against bf16.
+
+    The inputs are the bf16 workload, quantised on the GPU (fa_quantize_fp8: Q and K per row, V
+    transposed). The forward is timed on codes already resident in HBM; the conversion is timed
+    separately (algorithmic bytes: read bf16 once, write e4m3 once, 3 bytes per element).
+    """
+    w = configs.LONG_CAUSAL_16K
+    q, k, v, lens = inputs.make(w, dev)
+    o16 = torch.empty_like(q)
+    lse16 = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    fa.fa_fwd(q, k, v, o16, lse16, w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal), lens, None)
+    q8, sq = fa.quantize_fp8(q)
+    k8, sk = fa.quantize_fp8(k, kv_seqlens=lens)
+    vt8, sv = fa.quantize_fp8(v, kv_seqlens=lens, transpose=True)
+
+    def quant():
+        fa.fa_quantize_fp8(q, q8, sq, w.B, w.H, w.Nq, w.d, None, 0, None)
+        fa.fa_quantize_fp8(k, k8, sk, w.B, w.H, w.Nk, w.d, lens, 0, None)
+        fa.fa_quantize_fp8(v, vt8, sv, w.B, w.H, w.Nk, w.d, lens, 1, None)
+
+    nq = max(3, steps // 2)
+    tq, _ = time_launches(quant, nq, warmup, torch)
+    o8 = torch.empty_like(q)
+    lse8 = torch.empty_like(lse16)
+
+    def fstep():
+        fa.fa_fwd_fp8(q8, k8, vt8, sq, sk, sv, o8, lse8, w.B, w.H, w.Nq, w.Nk, w.d, w.scale,
+                      int(w.causal), lens, None)
+
+    t, per = time_launches(fstep, steps, warmup, torch)
+    avg = float(np.mean(per))
+    fl = w.counted_flops()
+    elems = 3 * w.B * w.H * w.Nq * w.d
+    diff = (o8.float() - o16.float())
+    rel = float(torch.linalg.vector_norm(diff) / torch.linalg.vector_norm(o16.float()))
+    out = {"workload": w.name, "unit": "TFLOP/s", "ms_per_step": round(t / steps * 1e3, 4),
+           "value": round(fl * steps / t / 1e12, 2), "counted_flops": fl,
+           "speedup_vs_bf16_forward": None,
+           "roofline": {"kernel": "prefill_fp8_kernel", "bound": "mfma", "achieved": round(fl / avg / 1e12, 2),
+                        "peak": PEAK_MFMA_FP8_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(fl / avg / 1e12 / PEAK_MFMA_FP8_TFLOPS, 4),
+                        "avg_launch_ms": round(avg * 1e3, 4)},
+           "conversion": {"kernels": "quant_amax_kernel + quant_rows_kernel / quant_transpose_kernel",
+                          "ms_per_call_qkv": round(tq / nq * 1e3, 4),
+                          "algorithmic_bytes": 3 * elems,
+                          "GBps": round(3 * elems * nq / tq / 1e9, 1)},
+           "error_vs_bf16_path": {"o_rel_frobenius": round(rel, 5),
+                                  "o_max_abs": round(float(diff.abs().max()), 5),
+                                  "lse_max_abs": round(float((lse8 - lse16).abs().max()), 5)}}
+    del q, k, v, q8, k8, vt8, o8, o16
+    torch.cuda.empty_cache()
+    return out
+
+
 def decode_bytes(w, lens) -> int:
     per_key = 2 * w.d * 2                      # one K row and one V row, bf16
     per_bh = 2 * w.d * 2 + 4                   # Q and O rows (bf16) and lse (fp32)
@@ -297,6 +355,8 @@ def main():
                     help="skip the sliding-window and packed-sequence timings")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass timing (fa_bwd)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the e4m3 forward timing (fa_quantize_fp8, fa_fwd_fp8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -391,6 +451,11 @@ def main():
 
     if not args.no_masks:
         result["masks"] = bench_masks(fa, configs, inputs, torch, dev, args.steps, args.warmup)
+
+    if not args.no_fp8:
+        result["fp8"] = bench_fp8(fa, configs, inputs, torch, dev, args.steps, args.warmup)
+        if w.name == configs.LONG_CAUSAL_16K.name:
+            result["fp8"]["speedup_vs_bf16_forward"] = round(result["ms_per_step"] / result["fp8"]["ms_per_step"], 3)
 
     if not args.no_backward:
         result["backward"] = bench_backward(fa, configs, inputs, torch, dev, args.steps, args.warmup)

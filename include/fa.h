@@ -144,6 +144,50 @@ int fa_std_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /* Bytes of workspace fa_std_fwd needs: 6 * B * H * Nq * ld (0 if any size is <= 0). */
 size_t fa_std_workspace_bytes(int B, int H, int Nq, int Nk);
 
+/*
+ * fa_quantize_fp8 -- e4m3 (OCP FP8: 4 exponent bits with bias 7, 3 mantissa bits, largest finite
+ * 448) quantisation of a bf16 tensor for fa_fwd_fp8. FP8 halves the bytes the forward pass moves
+ * and doubles the matrix-core rate, at the cost of a scaled conversion and, for V, a transpose
+ * (page "FlashAttention：把注意力从公式写成数据流", sections "用实验验证而不是背诵结论" and
+ * "精度、掩码和边界情况"). One scale per (b, h) slice: s = amax / 448 in fp32 over the slice's
+ * valid rows (rows at or past lens[b], clamped to [0, N], are excluded and stored as zero), s = 1
+ * for an all-zero slice; element x becomes e4m3(x / s), the quotient a correctly rounded fp32
+ * division and the conversion round-to-nearest-even. The values must be finite.
+ *   x        bf16 [B][H][N][d], 16-byte aligned.
+ *   y        e4m3 codes, 16-byte aligned: [B][H][N][d] when transpose == 0; the transpose
+ *            [B][H][d][fa_fp8_vt_cols(N)] when transpose == 1 (padding columns zero).
+ *   descale  fp32 [B*H], receives s per slice (dequantised value = s * e4m3 value).
+ *   lens     int32 [B] or NULL (all N rows valid). d in {64, 128}; N * d < 2^31; transposed
+ *            N <= 4194240.
+ * A workspace of 4 * B * H * min(64, max(1, N*d/32768)) bytes is allocated and freed
+ * stream-ordered on `stream`. Errors as for fa_fwd.
+ */
+int fa_quantize_fp8(const void* x, void* y, float* descale, int B, int H, int N, int d,
+                    const int32_t* lens, int transpose, void* stream);
+
+/* Columns of a transposed e4m3 V: Nk rounded up to a multiple of 64 (0 if Nk <= 0). */
+int fa_fp8_vt_cols(int Nk);
+
+/*
+ * fa_fwd_fp8 -- the attention forward of fa_fwd on e4m3 inputs (from fa_quantize_fp8): the
+ * result is that of fa_fwd's definition on the dequantised values s_q * q8, s_k * k8, s_v * v8,
+ * except that the probabilities are rounded to e4m3 (after scaling by 8) for the P V product, a
+ * weight error of at most 2^-4 P_ij + 2^-13 / l_i per pair (l_i = sum_j exp(S_ij - max_j S_ij)).
+ * Arithmetic: e4m3 x e4m3 products on the matrix cores with fp32 accumulation, softmax and the
+ * normaliser in fp32 (from the unrounded probabilities), O rounded to bf16 once.
+ *   q8       e4m3 [B][H][Nq][d]     k8  e4m3 [B][H][Nk][d]
+ *   vt8      e4m3 V^T [B][H][d][fa_fp8_vt_cols(Nk)]; it must hold no NaN code (0x7F, 0xFF) in
+ *            any column, padding included (fa_quantize_fp8 writes zeros there).
+ *   descale_q, descale_k, descale_v  fp32 [B*H] slice scales, or NULL for 1.
+ *   o        bf16 [B][H][Nq][d];    lse fp32 [B][H][Nq] (natural log, of the dequantised scores).
+ *   Other arguments and rules as for fa_fwd; q8, k8, vt8, o 16-byte aligned; one head's q8, k8
+ *   and vt8 below 2^31 bytes. Key rows of k8 at or past L_b are never read.
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, const float* descale_q,
+               const float* descale_k, const float* descale_v, void* o, float* lse,
+               int B, int H, int Nq, int Nk, int d, float scale, int causal,
+               const int32_t* kv_seqlens, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* fa_status_string(int status);
 

@@ -18,6 +18,11 @@ Entry points mirror the C ABI in ``include/fa.h``:
 * ``fa_std_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, workspace,
   workspace_bytes, stream)`` -- bf16, standard (materialising) algorithm, the baseline
 * ``fa_std_workspace_bytes(B, H, Nq, Nk)``
+* ``fa_quantize_fp8(x, y, descale, B, H, N, d, lens, transpose, stream)`` -- bf16 -> e4m3 with one
+  scale per (b, h) slice, V optionally transposed
+* ``fa_fp8_vt_cols(Nk)``
+* ``fa_fwd_fp8(q8, k8, vt8, descale_q, descale_k, descale_v, o, lse, B, H, Nq, Nk, d, scale,
+  causal, kv_seqlens, stream)`` -- e4m3 forward
 * ``fa_status_string(status)``, ``fa_last_error()``
 
 Pointer arguments accept a torch tensor (its ``data_ptr()``), an int address or None; ``stream``
@@ -26,7 +31,8 @@ accepts a ``torch.cuda.Stream``, an int handle or None (the current torch stream
 (``window=(left, right)`` selects ``fa_fwd_window``); ``varlen_attention`` does the same for
 packed sequences;
 ``standard_attention(q, k, v, ...)`` does the same for ``fa_std_fwd`` (bf16 only), allocating
-its workspace with torch unless one is passed.
+its workspace with torch unless one is passed. ``quantize_fp8`` and ``attention_fp8`` allocate
+the e4m3 tensors, scales and outputs for ``fa_quantize_fp8`` and ``fa_fwd_fp8``.
 """
 
 from __future__ import annotations
@@ -37,7 +43,8 @@ import os
 from typing import Optional, Tuple
 
 __all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_window", "fa_fwd_varlen", "fa_bwd",
-           "attention_backward", "fa_std_fwd",
+           "attention_backward", "fa_std_fwd", "fa_quantize_fp8", "fa_fp8_vt_cols", "fa_fwd_fp8",
+           "quantize_fp8", "attention_fp8",
            "fa_std_workspace_bytes", "fa_status_string", "fa_last_error", "attention",
            "varlen_attention", "standard_attention", "library_path", "load_library"]
 
@@ -87,6 +94,12 @@ def load_library():
     lib.fa_std_fwd.restype = ci
     lib.fa_std_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.fa_std_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_quantize_fp8.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp, ci, vp]
+    lib.fa_quantize_fp8.restype = ci
+    lib.fa_fp8_vt_cols.argtypes = [ci]
+    lib.fa_fp8_vt_cols.restype = ci
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp, vp]
+    lib.fa_fwd_fp8.restype = ci
     lib.fa_status_string.argtypes = [ci]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -236,6 +249,82 @@ def fa_std_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, work
                         _ptr(workspace), int(workspace_bytes), _stream(stream))
     if st != FA_OK:
         raise FaError(st, f"{fa_status_string(st)} ({fa_last_error()})")
+
+
+def _raise_on(st) -> None:
+    if st != FA_OK:
+        raise FaError(st, f"{fa_status_string(st)} ({fa_last_error()})")
+
+
+def fa_quantize_fp8(x, y, descale, B, H, N, d, lens=None, transpose=0, stream=None) -> None:
+    """bf16 -> e4m3 with one scale per (b, h) slice; see include/fa.h for the contract."""
+    lib = load_library()
+    _raise_on(lib.fa_quantize_fp8(_ptr(x), _ptr(y), _ptr(descale), int(B), int(H), int(N), int(d),
+                                  _ptr(lens), int(transpose), _stream(stream)))
+
+
+def fa_fp8_vt_cols(Nk) -> int:
+    """Columns of a transposed e4m3 V (Nk rounded up to 64)."""
+    return int(load_library().fa_fp8_vt_cols(int(Nk)))
+
+
+def fa_fwd_fp8(q8, k8, vt8, descale_q, descale_k, descale_v, o, lse, B, H, Nq, Nk, d, scale, causal,
+               kv_seqlens=None, stream=None) -> None:
+    """e4m3 forward; see include/fa.h for the contract."""
+    lib = load_library()
+    _raise_on(lib.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), _ptr(descale_q), _ptr(descale_k),
+                             _ptr(descale_v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
+                             int(d), float(scale), int(causal), _ptr(kv_seqlens), _stream(stream)))
+
+
+def quantize_fp8(x, kv_seqlens=None, transpose: bool = False, stream=None):
+    """(codes, descale) for a contiguous bf16 device tensor x [B, H, N, d]: codes uint8
+    [B, H, N, d], or [B, H, d, fa_fp8_vt_cols(N)] when transpose; descale fp32 [B, H]."""
+    import torch
+
+    if x.dim() != 4 or x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 device tensor [B, H, N, d]")
+    B, H, N, d = x.shape
+    if kv_seqlens is not None and (kv_seqlens.dtype != torch.int32 or not kv_seqlens.is_cuda
+                                   or kv_seqlens.numel() != B):
+        raise ValueError("kv_seqlens must be an int32 device tensor of length B")
+    shape = (B, H, d, fa_fp8_vt_cols(N)) if transpose else (B, H, N, d)
+    y = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    descale = torch.empty((B, H), dtype=torch.float32, device=x.device)
+    fa_quantize_fp8(x, y, descale, B, H, N, d, kv_seqlens, int(bool(transpose)), stream)
+    return y, descale
+
+
+def attention_fp8(q8, k8, vt8, descale_q, descale_k, descale_v, scale: Optional[float] = None,
+                  causal: bool = False, kv_seqlens=None, out=None, lse=None,
+                  stream=None) -> Tuple["object", "object"]:
+    """O (bf16) and lse for e4m3 q8 [B,H,Nq,d], k8 [B,H,Nk,d], vt8 [B,H,d,fa_fp8_vt_cols(Nk)]."""
+    import torch
+
+    if q8.dim() != 4 or k8.dim() != 4 or vt8.dim() != 4:
+        raise ValueError("q8, k8, vt8 must be 4-d")
+    B, H, Nq, d = q8.shape
+    Nk = k8.shape[2]
+    if tuple(k8.shape) != (B, H, Nk, d) or tuple(vt8.shape) != (B, H, d, fa_fp8_vt_cols(Nk)):
+        raise ValueError("k8 must be [B, H, Nk, d] and vt8 [B, H, d, fa_fp8_vt_cols(Nk)]")
+    for t in (q8, k8, vt8):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q8, k8, vt8 must be contiguous uint8 device tensors")
+    for t in (descale_q, descale_k, descale_v):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != B * H or not t.is_cuda):
+            raise ValueError("descales must be fp32 device tensors of B*H entries (or None)")
+    if kv_seqlens is not None and (kv_seqlens.dtype != torch.int32 or not kv_seqlens.is_cuda
+                                   or kv_seqlens.numel() != B):
+        raise ValueError("kv_seqlens must be an int32 device tensor of length B")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device)
+    fa_fwd_fp8(q8, k8, vt8, descale_q, descale_k, descale_v, out, lse, B, H, Nq, Nk, d, scale,
+               int(bool(causal)), kv_seqlens, stream)
+    return out, lse
 
 
 def _check_qkv(q, k, v, kv_seqlens, dtypes):

@@ -18,7 +18,7 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
 SOURCES = ["fa_prefill_bf16.hip", "fa_prefill_pp.hip", "fa_prefill_f32.hip", "fa_decode.hip", "fa_standard.hip",
-           "fa_backward.hip", "fa_api.cpp"]
+           "fa_backward.hip", "fa_quant_fp8.hip", "fa_prefill_fp8.hip", "fa_api.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -1,6 +1,7 @@
 // fa_api.cpp -- the C ABI of libfa: argument checks, dispatch and launches (host side).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -17,6 +18,9 @@ hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream)
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_standard(const StandardParams& p, int d, hipStream_t stream);
 hipError_t launch_backward(const BackwardParams& p, int d, hipStream_t stream);
+hipError_t launch_quantize_fp8(const QuantParams& p, hipStream_t stream);
+hipError_t launch_prefill_fp8(const PrefillFp8Params& p, int d, hipStream_t stream);
+int prefill_fp8_rows_per_wg();
 int prefill_bf16_rows_per_wg(int d);
 int prefill_bf16_pp_rows_per_wg();
 constexpr int kPrefillLongNq = 2048;  // query rows from which the 8-wave prefill kernel is used
@@ -354,3 +358,88 @@ extern "C" const char* fa_status_string(int status) {
 }
 
 extern "C" const char* fa_last_error(void) { return g_last_error; }
+
+extern "C" int fa_fp8_vt_cols(int Nk) { return Nk <= 0 ? 0 : (int)(((int64_t)Nk + 63) / 64 * 64); }
+
+extern "C" int fa_quantize_fp8(const void* x, void* y, float* descale, int B, int H, int N, int d,
+                               const int32_t* lens, int transpose, void* stream) {
+  g_last_error[0] = '\0';
+  if (B < 0 || H < 0 || N < 0) return fail(FA_ERR_INVALID_ARGUMENT, "B, H, N must be >= 0");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d must be 64 or 128");
+  if (transpose != 0 && transpose != 1) return fail(FA_ERR_INVALID_ARGUMENT, "transpose must be 0 or 1");
+  if ((int64_t)N * d >= ((int64_t)1 << 31)) return fail(FA_ERR_UNSUPPORTED, "one slice must hold fewer than 2^31 elements");
+  const int64_t bh = (int64_t)B * H;
+  if (bh > std::numeric_limits<int32_t>::max()) return fail(FA_ERR_UNSUPPORTED, "B*H exceeds int32");
+  if (bh == 0) return FA_OK;
+  if (!descale || (N > 0 && (!x || !y))) return fail(FA_ERR_INVALID_ARGUMENT, "x, y and descale must be non-null");
+  if ((x && !aligned(x, 16)) || (y && !aligned(y, 16)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned");
+  if (!aligned(descale, 4) || (lens && !aligned(lens, 4)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "descale and lens must be 4-byte aligned");
+  fa::QuantParams p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.y = static_cast<uint8_t*>(y);
+  p.descale = descale;
+  p.lens = lens;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.D = d;
+  p.transpose = transpose;
+  p.cols = transpose ? fa_fp8_vt_cols(N) : 0;
+  if (transpose && p.cols / 64 > 65535)
+    return fail(FA_ERR_UNSUPPORTED, "N too large for the transposed layout (at most 4194240 rows)");
+  // Chunks of about 64 KiB of input for the amax pass, at most 64 per slice.
+  const int64_t bytes = (int64_t)N * d * 2;
+  p.n_chunks = (int)std::min<int64_t>(64, std::max<int64_t>(1, bytes / 65536));
+  p.rows_per_chunk = std::max(1, (N + p.n_chunks - 1) / p.n_chunks);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, (size_t)bh * p.n_chunks * sizeof(float), s);
+  if (e != hipSuccess) return fail_hip(e, "hipMallocAsync(quantiser workspace)");
+  p.partial = static_cast<float*>(ws);
+  e = fa::launch_quantize_fp8(p, s);
+  hipError_t ef = hipFreeAsync(ws, s);
+  if (e == hipSuccess) e = ef;
+  if (e != hipSuccess) return fail_hip(e, "quantiser launch");
+  return FA_OK;
+}
+
+extern "C" int fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, const float* descale_q,
+                          const float* descale_k, const float* descale_v, void* o, float* lse,
+                          int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                          const int32_t* kv_seqlens, void* stream) {
+  int st = check_common(q8, k8, vt8, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens);
+  if (st == 1) return FA_OK;
+  if (st != FA_OK) return st;
+  if ((descale_q && !aligned(descale_q, 4)) || (descale_k && !aligned(descale_k, 4)) ||
+      (descale_v && !aligned(descale_v, 4)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "descale arrays must be 4-byte aligned");
+  // Per-(b, h) buffer views are addressed with 32-bit byte offsets.
+  if ((int64_t)fa_fp8_vt_cols(Nk) * d >= ((int64_t)1 << 31) || (int64_t)Nq * d >= ((int64_t)1 << 31))
+    return fail(FA_ERR_UNSUPPORTED, "one head's q8, k8 or vt8 must stay below 2^31 bytes");
+  const int bm = fa::prefill_fp8_rows_per_wg();
+  const int64_t n_wg = (int64_t)B * H * ((Nq + bm - 1) / bm);
+  if (n_wg > std::numeric_limits<int32_t>::max()) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  fa::PrefillFp8Params p{};
+  p.q = static_cast<const uint8_t*>(q8);
+  p.k = static_cast<const uint8_t*>(k8);
+  p.vt = static_cast<const uint8_t*>(vt8);
+  p.dq = descale_q;
+  p.dk = descale_k;
+  p.dv = descale_v;
+  p.o = o;
+  p.lse = lse;
+  p.kv_seqlens = kv_seqlens;
+  p.B = B;
+  p.H = H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.ldv = fa_fp8_vt_cols(Nk);
+  p.c = (float)((double)scale * 1.4426950408889634);
+  if (p.c == 0.0f) p.c = 1e-30f;  // as in the bf16 path: the results of c = 0
+  p.causal = causal;
+  hipError_t e = fa::launch_prefill_fp8(p, d, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "fp8 prefill launch");
+  return FA_OK;
+}

@@ -74,4 +74,37 @@ struct StandardParams {
   int causal;
 };
 
+// e4m3 quantisation of a bf16 tensor with one scale per (b, h) slice (rows of the slice past
+// its sequence's length are excluded from the scale and stored as zero).
+struct QuantParams {
+  const uint16_t* x;      // [B][H][N][D] bf16
+  uint8_t* y;             // [B][H][N][D] e4m3, or [B][H][D][cols] when transpose
+  float* descale;         // [B*H] the scale s of each slice
+  float* partial;         // [B*H][n_chunks] workspace: amax of each chunk of rows
+  const int32_t* lens;    // [B] valid rows per sequence, or nullptr
+  int B, H, N, D;
+  int cols;               // transposed row length: N rounded up to 64
+  int n_chunks;           // row chunks per slice for the amax pass (1..64)
+  int rows_per_chunk;
+  int transpose;
+};
+
+// FP8 (e4m3) forward: Q, K as [B][H][N][D] codes, V as V^T [B][H][D][ldv] codes, one scale per
+// (b, h) slice of each; output and lse as in the bf16 forward.
+struct PrefillFp8Params {
+  const uint8_t* q;       // [B][H][Nq][D]
+  const uint8_t* k;       // [B][H][Nk][D]
+  const uint8_t* vt;      // [B][H][D][ldv]
+  const float* dq;        // [B*H] scales (nullptr: 1)
+  const float* dk;
+  const float* dv;
+  void* o;                // [B][H][Nq][D] bf16
+  float* lse;             // [B][H][Nq]
+  const int32_t* kv_seqlens;
+  int B, H, Nq, Nk, ldv;
+  float c;                // scale * log2(e)
+  int causal;
+  int n_qtiles, n_tiles;
+};
+
 }  // namespace fa

@@ -1,0 +1,262 @@
+"""GPU parity of the FP8 (e4m3) path, through the C ABI, against the CPU oracle.
+
+* fa_quantize_fp8 against oracle.fp8.quantize_e4m3: codes and scales bit-exact (the integer
+  decision e4m3(x / s) is taken in fp32 on both sides), row and transposed layouts, lengths,
+  poisoned rows past the length, all-zero slices.
+* fa_fwd_fp8 against oracle.fp8.attention_fwd_fp8 (exact attention of the dequantised values) on
+  codes made by the oracle's quantiser from seeded inputs. The GPU path rounds the probabilities to
+  e4m3 before P V, so O is held to a tolerance built from the oracle's per-pair bound b_ij on that
+  rounding (oracle.fp8.p_rounding_bound):
+    elementwise |O - O_ref|_ic <= sum_j b_ij |V_jc| + 2^-8 |O_ref_ic| + 1e-4 sum_j P_ij |V_jc| + 1e-6
+    (rigorous: rounding bound, plus bf16 output rounding and fp32 accumulation);
+    ||O - O_ref||_F <= 2 sqrt(sum_ic sum_j b_ij^2 V_jc^2 / 3) + 2^-8 ||O_ref||_F + 1e-6
+    (the rounding errors are independent and at most b_ij, so their variance is at most b^2/3);
+  lse comes from the unrounded probabilities: the bf16 path's 1e-3 plus the score error below.
+  Cases where no rounding happens (Q = 0: every scaled probability is exactly 8; one allowed key)
+  get b = 0, so O must match to output rounding.
+
+The fp8 matrix instruction also does not sum its 64 products exactly: with one allowed key per
+row (lse = the score itself) its dot products were measured on MI355X to be off by up to 2^-15.2
+of sum_d |q_d k_d| on normal inputs and 2^-11.7 on inputs spread over 16 binades. The tolerance
+takes EPS_DOT = 2^-11 of that sum as the score error delta_ij (times |scale|); a score error
+delta moves lse by at most max_j delta_ij and a weight by at most (e^(2 delta) - 1) P_ij, and the
+P V product adds EPS_DOT sum_j P_ij |V_jc|. Those terms are added to both O limits and to lse's.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_exact_23_amd as fa
+from io_aware_exact_23_amd import configs, inputs
+from oracle import fp8 as ofp8
+
+from parity_util import to_f64
+
+EPS_DOT = 2.0 ** -11
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load_library()
+
+
+def _quantize_gpu(x, lens=None, transpose=False):
+    y, s = fa.quantize_fp8(x, kv_seqlens=lens, transpose=transpose)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), s.cpu().numpy()
+
+
+QUANT_CASES = [
+    # B, H, N, d, lens, std
+    (2, 3, 70, 64, None, 1.0),
+    (2, 3, 70, 64, [70, 33], 2.0),
+    (1, 2, 300, 128, None, 0.5),
+    (3, 2, 1000, 128, [1000, 1, 0], 1.0),
+    (2, 2, 4097, 64, [4097, 2000], 3.0),
+    (1, 1, 64, 128, None, 1e-3),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,lens,std", QUANT_CASES)
+@pytest.mark.parametrize("transpose", [False, True])
+def test_quantizer_bit_exact(B, H, N, d, lens, std, transpose):
+    x = inputs.normal((B, H, N, d), 7 * N + d + B, DEV, "bf16", std)
+    lt = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    if lt is not None:
+        inputs.fill_padding(x, lt.cpu(), float("nan"))  # never read
+    y, s = _quantize_gpu(x, lt, transpose)
+    yr, sr = ofp8.quantize_e4m3(np.nan_to_num(to_f64(x)), kv_seqlens=lens, transpose=transpose)
+    print(f"quantise {B}x{H}x{N}x{d} lens={lens} transpose={transpose}", flush=True)
+    assert np.array_equal(s, sr), "scales differ"
+    bad = np.argwhere(y != yr)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}"
+
+
+def test_quantizer_zero_slice_and_empty():
+    x = inputs.normal((2, 2, 100, 64), 5, DEV, "bf16")
+    x[1, 0] = 0
+    y, s = _quantize_gpu(x)
+    assert s[1, 0] == 1.0 and np.all(y[1, 0] == 0)
+    e = torch.empty((2, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    y, s = _quantize_gpu(e, transpose=True)
+    assert y.shape == (2, 2, 64, 0) and np.all(s == 1.0)
+
+
+def _make_fp8(B, H, Nq, Nk, d, seed, std=1.0, lens=None):
+    """Seeded bf16 inputs quantised by the oracle; codes and scales uploaded for the GPU."""
+    q = to_f64(inputs.normal((B, H, Nq, d), seed, "cpu", "bf16", std))
+    k = to_f64(inputs.normal((B, H, Nk, d), seed + 1, "cpu", "bf16", std))
+    v = to_f64(inputs.normal((B, H, Nk, d), seed + 2, "cpu", "bf16", 1.0))
+    q8, sq = ofp8.quantize_e4m3(q)
+    k8, sk = ofp8.quantize_e4m3(k, kv_seqlens=lens)
+    vt8, sv = ofp8.quantize_e4m3(v, kv_seqlens=lens, transpose=True)
+    return q8, k8, vt8, sq, sk, sv
+
+
+def _run_fp8(q8, k8, vt8, sq, sk, sv, scale, causal=False, lens=None):
+    g = [torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in (q8, k8, vt8, sq, sk, sv)]
+    lt = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o, lse = fa.attention_fp8(*g, scale=scale, causal=causal, kv_seqlens=lt)
+    torch.cuda.synchronize()
+    return to_f64(o), to_f64(lse)
+
+
+def check_fp8(o, lse, q8, k8, vt8, sq, sk, sv, scale, causal, lens, rows=None, exact=False, what=""):
+    """O and lse against the oracle with the tolerance derived from the P rounding bound."""
+    res = ofp8.attention_fwd_fp8(q8, k8, vt8, sq, sk, sv, scale, causal=causal, kv_seqlens=lens,
+                                 rows=rows, return_p=True)
+    o_ref, lse_ref, p = res
+    nk = np.asarray(k8).shape[2]
+    v = ofp8.dequantize_e4m3(vt8, sv, transposed=True, n=nk)
+    va = np.abs(v)
+    # Score error bound per row: EPS_DOT * |scale| * max over allowed keys of sum_d |q_d k_d|.
+    qd = np.abs(ofp8.dequantize_e4m3(q8, sq))
+    if rows is not None:
+        qd = qd[:, :, rows]
+    kd = np.abs(ofp8.dequantize_e4m3(k8, sk))
+    smag = np.where(p > 0, qd @ np.swapaxes(kd, 2, 3), 0.0)
+    delta = EPS_DOT * abs(float(scale)) * smag.max(axis=-1, initial=0.0)   # (B, H, R)
+    pv = p @ va
+    dot_term = (np.expm1(2.0 * delta)[..., None] + 2.0 * EPS_DOT) * pv
+    bnd = np.zeros_like(p) if exact else ofp8.p_rounding_bound(p)
+    tol = bnd @ va + dot_term + 2.0 ** -8 * np.abs(o_ref) + 1e-4 * pv + 1e-6
+    err = np.abs(o - o_ref)
+    over = err > tol
+    assert not over.any(), (f"{what}: {int(over.sum())} elements past the bound, worst excess "
+                            f"{float(np.max(err - tol)):.3e} at {np.argwhere(over)[0].tolist()}")
+    stat = np.sqrt(np.sum((bnd ** 2) @ (va ** 2)) / 3.0)
+    fro = float(np.sqrt(np.sum(err ** 2)))
+    lim = (2.0 * stat + float(np.sqrt(np.sum(dot_term ** 2)))
+           + 2.0 ** -8 * float(np.sqrt(np.sum(o_ref ** 2))) + 1e-6)
+    assert fro <= lim, f"{what}: ||O - O_ref|| {fro:.4e} > {lim:.4e}"
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse), fin), f"{what}: lse finiteness differs"
+    assert np.all(lse[~fin] == lse_ref[~fin])
+    if fin.any():
+        le = np.abs(lse[fin] - lse_ref[fin])
+        ltol = 1e-3 + delta[fin]
+        assert np.all(le <= ltol), f"{what}: lse error {float(le.max()):.3e} (bound {float(ltol[np.argmax(le)]):.3e})"
+    rel = fro / max(float(np.sqrt(np.sum(o_ref ** 2))), 1e-30)
+    print(f"{what}: max|dO| {float(err.max()):.3e}  rel Frobenius {rel:.3e}  (bound {lim:.3e})", flush=True)
+
+
+SHAPES = [
+    # B, H, Nq, Nk, d, causal, lens
+    (1, 1, 17, 17, 64, True, None),
+    (2, 3, 100, 300, 128, False, None),
+    (1, 2, 257, 257, 128, True, None),
+    (2, 2, 300, 300, 64, True, [300, 77]),
+    (2, 1, 200, 333, 64, False, [1, 333]),
+    (3, 2, 600, 600, 128, True, None),
+    (2, 2, 2, 65, 128, False, [65, 3]),
+    (2, 3, 1, 700, 128, False, [700, 5]),
+    (1, 2, 1000, 1000, 128, True, None),
+    (1, 1, 520, 2100, 64, False, [2100]),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal,lens", SHAPES)
+def test_fp8_shapes(B, H, Nq, Nk, d, causal, lens):
+    q8, k8, vt8, sq, sk, sv = _make_fp8(B, H, Nq, Nk, d, seed=11 * Nq + Nk + d, lens=lens)
+    o, lse = _run_fp8(q8, k8, vt8, sq, sk, sv, d ** -0.5, causal, lens)
+    check_fp8(o, lse, q8, k8, vt8, sq, sk, sv, d ** -0.5, causal, lens,
+              what=f"fp8 {B}x{H}x{Nq}x{Nk} d={d} causal={causal} lens={lens}")
+
+
+def test_fp8_zero_query_is_exact_mean():
+    # Q = 0: every score is 0, every scaled probability exactly 8 (no e4m3 rounding), O = mean of
+    # the allowed V rows, times s_v.
+    B, H, N, d = 2, 2, 300, 128
+    q8, k8, vt8, sq, sk, sv = _make_fp8(B, H, N, N, d, seed=21, lens=[300, 150])
+    q8[:] = 0
+    for causal in (False, True):
+        o, lse = _run_fp8(q8, k8, vt8, sq, sk, sv, 0.3, causal, [300, 150])
+        check_fp8(o, lse, q8, k8, vt8, sq, sk, sv, 0.3, causal, [300, 150], exact=True,
+                  what=f"fp8 Q=0 causal={causal}")
+
+
+def test_fp8_one_key_returns_its_value():
+    q8, k8, vt8, sq, sk, sv = _make_fp8(2, 2, 70, 90, 64, seed=31, lens=[1, 90])
+    o, lse = _run_fp8(q8, k8, vt8, sq, sk, sv, 0.125, False, [1, 1])
+    check_fp8(o, lse, q8, k8, vt8, sq, sk, sv, 0.125, False, [1, 1], exact=True, what="fp8 one key")
+
+
+def test_fp8_no_keys_and_empty_sequences():
+    q8, k8, vt8, sq, sk, sv = _make_fp8(3, 2, 40, 70, 128, seed=41, lens=[0, 1, 70])
+    o, lse = _run_fp8(q8, k8, vt8, sq, sk, sv, 0.1, False, [0, 1, 70])
+    check_fp8(o, lse, q8, k8, vt8, sq, sk, sv, 0.1, False, [0, 1, 70], what="fp8 empty sequences")
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+    q8, k8, vt8, sq, sk, sv = _make_fp8(2, 1, 5, 0, 64, seed=43)
+    o, lse = _run_fp8(q8, k8, vt8, sq, sk, sv, 0.1, False, None)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def test_fp8_large_and_negative_scores():
+    q8, k8, vt8, sq, sk, sv = _make_fp8(2, 2, 300, 300, 64, seed=51, std=4.0)
+    for scale in (2.0, -0.7):
+        o, lse = _run_fp8(q8, k8, vt8, sq, sk, sv, scale, True, None)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        check_fp8(o, lse, q8, k8, vt8, sq, sk, sv, scale, True, None, what=f"fp8 scale={scale}")
+
+
+def test_fp8_null_scales_mean_one():
+    q8, k8, vt8, _, _, _ = _make_fp8(1, 2, 130, 130, 64, seed=61)
+    g = [torch.from_numpy(a).to(DEV) for a in (q8, k8, vt8)]
+    o, lse = fa.attention_fp8(*g, None, None, None, scale=0.2, causal=True)
+    torch.cuda.synchronize()
+    ones = np.ones((1, 2), dtype=np.float32)
+    check_fp8(to_f64(o), to_f64(lse), q8, k8, vt8, ones, ones, ones, 0.2, True, None, what="fp8 unit scales")
+
+
+def test_fp8_padding_rows_of_k_are_never_read():
+    # K codes past the length poisoned with NaN codes; V^T past the length is zero (quantiser).
+    lens = [300, 45, 129]
+    q8, k8, vt8, sq, sk, sv = _make_fp8(3, 2, 150, 300, 128, seed=71, lens=lens)
+    o1, l1 = _run_fp8(q8, k8, vt8, sq, sk, sv, 0.1, False, lens)
+    k8p = k8.copy()
+    for b, L in enumerate(lens):
+        k8p[b, :, L:] = 0x7F
+    o2, l2 = _run_fp8(q8, k8p, vt8, sq, sk, sv, 0.1, False, lens)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_fp8_quantize_then_attend_on_gpu_matches_oracle_chain():
+    # The whole GPU chain (fa_quantize_fp8 then fa_fwd_fp8) against the oracle's chain.
+    B, H, N, d = 2, 2, 513, 128
+    q = inputs.normal((B, H, N, d), 81, DEV, "bf16")
+    k = inputs.normal((B, H, N, d), 82, DEV, "bf16")
+    v = inputs.normal((B, H, N, d), 83, DEV, "bf16")
+    q8, sq = fa.quantize_fp8(q)
+    k8, sk = fa.quantize_fp8(k)
+    vt8, sv = fa.quantize_fp8(v, transpose=True)
+    o, lse = fa.attention_fp8(q8, k8, vt8, sq, sk, sv, scale=d ** -0.5, causal=True)
+    torch.cuda.synchronize()
+    rq8, rsq = ofp8.quantize_e4m3(to_f64(q))
+    rk8, rsk = ofp8.quantize_e4m3(to_f64(k))
+    rvt8, rsv = ofp8.quantize_e4m3(to_f64(v), transpose=True)
+    check_fp8(to_f64(o), to_f64(lse), rq8, rk8, rvt8, rsq, rsk, rsv, d ** -0.5, True, None,
+              what="fp8 GPU chain")
+
+
+def test_fp8_long_causal_workload_sampled_rows():
+    # The 16K causal shape at full size: every (b, h), sampled query rows including the first, the
+    # last and rows at tile edges.
+    w = configs.LONG_CAUSAL_16K
+    q = to_f64(inputs.normal((w.B, w.H, w.Nq, w.d), w.seed, "cpu", "bf16", w.input_std))
+    k = to_f64(inputs.normal((w.B, w.H, w.Nk, w.d), w.seed + 1, "cpu", "bf16", w.input_std))
+    v = to_f64(inputs.normal((w.B, w.H, w.Nk, w.d), w.seed + 2, "cpu", "bf16", 1.0))
+    q8, sq = ofp8.quantize_e4m3(q)
+    k8, sk = ofp8.quantize_e4m3(k)
+    vt8, sv = ofp8.quantize_e4m3(v, transpose=True)
+    del q, k, v
+    o, lse = _run_fp8(q8, k8, vt8, sq, sk, sv, w.scale, True, None)
+    rows = np.array([0, 1, 63, 64, 255, 256, 4095, 8191, 8192, 12345, 16127, 16128, 16383])
+    check_fp8(o[:, :, rows], lse[:, :, rows], q8, k8, vt8, sq, sk, sv, w.scale, True, None,
+              rows=rows, what="fp8 " + w.name)

@@ -23,8 +23,9 @@ def declared_functions():
 
 
 def test_header_declares_the_abi():
-    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_f32", "fa_fwd_varlen", "fa_fwd_window",
-                                    "fa_last_error", "fa_status_string", "fa_std_fwd",
+    assert declared_functions() == ["fa_bwd", "fa_fp8_vt_cols", "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8",
+                                    "fa_fwd_varlen", "fa_fwd_window", "fa_last_error",
+                                    "fa_quantize_fp8", "fa_status_string", "fa_std_fwd",
                                     "fa_std_workspace_bytes"]
 
 
@@ -236,3 +237,69 @@ def test_backward_empty_is_a_no_op(args):
     call.update(args)
     fa.fa_bwd(**call)
     assert fa.fa_last_error() == ""
+
+
+FP8 = dict(q8=A, k8=A, vt8=A, descale_q=A, descale_k=A, descale_v=A, o=A, lse=A, B=2, H=3, Nq=8,
+           Nk=8, d=64, scale=0.125, causal=0, kv_seqlens=None, stream=0)
+
+
+@needs_lib
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED, "64 or 128"),
+    (dict(Nq=-1), fa.FA_ERR_INVALID_ARGUMENT, ">= 0"),
+    (dict(causal=1, Nq=4, Nk=5), fa.FA_ERR_UNSUPPORTED, "Nq == Nk"),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARGUMENT, "0 or 1"),
+    (dict(q8=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(vt8=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(vt8=A + 8), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(descale_k=A + 2), fa.FA_ERR_INVALID_ARGUMENT, "4-byte aligned"),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARGUMENT, "finite"),
+])
+def test_fp8_forward_argument_errors(args, status, needle):
+    call = dict(FP8)
+    call.update(args)
+    with pytest.raises(fa.FaError) as ei:
+        fa.fa_fwd_fp8(**call)
+    assert ei.value.status == status
+    assert needle in ei.value.message
+
+
+@needs_lib
+@pytest.mark.parametrize("args", [dict(B=0), dict(H=0), dict(Nq=0), dict(Nq=0, Nk=0)])
+def test_fp8_forward_empty_is_a_no_op(args):
+    call = dict(FP8)
+    call.update(args)
+    fa.fa_fwd_fp8(**call)
+    assert fa.fa_last_error() == ""
+
+
+QUANT = dict(x=A, y=A, descale=A, B=2, H=3, N=100, d=128, lens=None, transpose=0, stream=0)
+
+
+@needs_lib
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED, "64 or 128"),
+    (dict(N=-5), fa.FA_ERR_INVALID_ARGUMENT, ">= 0"),
+    (dict(transpose=2), fa.FA_ERR_INVALID_ARGUMENT, "0 or 1"),
+    (dict(x=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(descale=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(y=A + 8), fa.FA_ERR_INVALID_ARGUMENT, "16-byte aligned"),
+    (dict(descale=A + 2), fa.FA_ERR_INVALID_ARGUMENT, "4-byte aligned"),
+    (dict(N=5000000, transpose=1), fa.FA_ERR_UNSUPPORTED, "transposed"),
+])
+def test_quantize_argument_errors(args, status, needle):
+    call = dict(QUANT)
+    call.update(args)
+    with pytest.raises(fa.FaError) as ei:
+        fa.fa_quantize_fp8(**call)
+    assert ei.value.status == status
+    assert needle in ei.value.message
+
+
+@needs_lib
+def test_quantize_empty_batch_and_vt_cols():
+    call = dict(QUANT)
+    call.update(B=0)
+    fa.fa_quantize_fp8(**call)
+    assert fa.fa_last_error() == ""
+    assert [fa.fa_fp8_vt_cols(n) for n in (0, 1, 63, 64, 65, 16384)] == [0, 64, 64, 64, 128, 16384]
