@@ -43,16 +43,23 @@ METRIC = "attention fwd TFLOP/s (bf16) and % of MFMA peak; decode HBM GB/s"
 PEAK_MFMA_BF16_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_MFMA_FP8_TFLOPS = 5033.2    # MI355X dense fp8: 256 CU x 2.4 GHz x 8192 FLOP/clk
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
-KERNEL_SOURCES = ["fa_prefill_bf16.hip", "fa_prefill_pp.hip", "fa_decode.hip", "fa_device.h", "fa_softmax.h",
-                  "fa_params.h", "fa_api.cpp"]
+# Sources each profiled kernel is built from: a committed counter summary counts for the current
+# build only if the hash of its kernel's sources matches.
+_COMMON = ["fa_device.h", "fa_params.h"]
+KERNEL_SOURCES = {
+    "prefill_bf16_pp_kernel": ["fa_prefill_pp.hip", "fa_softmax.h"] + _COMMON,
+    "prefill_bf16_kernel": ["fa_prefill_bf16.hip", "fa_softmax.h"] + _COMMON,
+    "decode_split_kernel": ["fa_decode.hip"] + _COMMON,
+    "prefill_fp8_kernel": ["fa_prefill_fp8.hip"] + _COMMON,
+}
 PREFILL_WORKLOADS = ["gpt2s_causal_b8_h12_n1024_d64", "bertl_padded_b16_h16_n512_d64",
                      "long_causal_b2_h16_n16384_d128"]
 LONG_NQ = 2048  # fa_fwd runs prefill_bf16_pp_kernel from this many query rows on
 
 
-def source_sha() -> str:
+def source_sha(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "io_aware_exact_23_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -323,7 +330,9 @@ def bench_fp8(fa, configs, inputs, torch, dev, steps, warmup):
            "roofline": {"kernel": "prefill_fp8_kernel", "bound": "mfma", "achieved": round(fl / avg / 1e12, 2),
                         "peak": PEAK_MFMA_FP8_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(fl / avg / 1e12 / PEAK_MFMA_FP8_TFLOPS, 4),
-                        "avg_launch_ms": round(avg * 1e3, 4)},
+                        "avg_launch_ms": round(avg * 1e3, 4),
+                        "traffic": traffic_from_profile("prefill_fp8_kernel", w.name,
+                                                        source_sha("prefill_fp8_kernel"))},
            "conversion": {"kernels": "quant_amax_kernel + quant_rows_kernel / quant_transpose_kernel",
                           "ms_per_call_qkv": round(tq / nq * 1e3, 4),
                           "algorithmic_bytes": 3 * elems,
@@ -392,7 +401,6 @@ def main():
     value = flops * args.steps / total / 1e12
     avg_launch = float(np.mean(per))
     achieved = flops / avg_launch / 1e12
-    sha = source_sha()
     if w.Nq == 1:
         kernel = "decode_split_kernel"
     else:
@@ -418,8 +426,8 @@ def main():
                      "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4),
                      "avg_launch_ms": round(avg_launch * 1e3, 4),
-                     "traffic": traffic_from_profile(kernel, w.name, sha),
-                     "source_sha": sha},
+                     "traffic": traffic_from_profile(kernel, w.name, source_sha(kernel)),
+                     "source_sha": source_sha(kernel)},
     }
 
     if not args.no_decode:
@@ -445,7 +453,8 @@ def main():
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(nbytes / davg / 1e9 / PEAK_HBM_GBS, 4),
                          "avg_launch_ms": round(davg * 1e3, 4),
-                         "traffic": traffic_from_profile("decode_split_kernel", wd.name, sha)},
+                         "traffic": traffic_from_profile("decode_split_kernel", wd.name,
+                                                         source_sha("decode_split_kernel"))},
         }
         del dq, dk, dv, do
 
