@@ -11,8 +11,9 @@
 //   bwd_delta_kernel  D_i = dO_i . O_i for every query row (fp32);
 //   bwd_dq_kernel     one workgroup of 4 waves per 128 query rows, K/V tiles through LDS as in
 //                     the forward kernel: S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T;
-//   bwd_dkdv_kernel   one workgroup of 4 waves per 128 keys, Q/dO tiles through LDS: S = Q K^T,
-//                     dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS.
+//   bwd_dkdv_kernel   one workgroup of 8 waves per 128 keys, Q/dO tiles through LDS; per SIMD
+//                     one wave computes S = Q K^T, P and dV^T += dO^T P, its partner dP = dO V^T,
+//                     then (taking P through LDS) dS and dK^T += Q^T dS.
 // Splitting dQ from dK/dV recomputes S and dP once more (7 matrix products per tile pair instead
 // of 5) but needs no atomics and gives run-to-run identical gradients. All products are bf16 on
 // the matrix cores with fp32 accumulation; P and dS are rounded to bf16 before their products,
@@ -27,6 +28,8 @@
 #include "fa_device.h"
 #include "fa_params.h"
 
+#include <type_traits>
+
 namespace fa {
 
 // Row of a 32-row block read by accumulator row r (an involution: swap bits 2 and 3).
@@ -38,6 +41,20 @@ template <int N>
 __device__ __forceinline__ void bwd_wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
+// Workgroup barrier that waits only for this wave's LDS accesses (lgkmcnt 0, vmcnt untouched):
+// __syncthreads() would also drain every vector-memory load in flight, including the next tile's
+// copies, and so serialise the prefetch. A wave waits for its own tile copies explicitly before
+// the barrier that publishes them. The empty asm keeps the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void bwd_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt 63 (no wait), expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
 }
 
 // ---- D_i = dO_i . O_i (fp32), one wave per row, 8 bf16 per lane and step.
@@ -70,22 +87,37 @@ struct BwdCfg {
   static constexpr int kKiBPerWave = kTileBytes / 1024 / 4;
 };
 
-// Per-lane byte offsets of the direct HBM -> LDS copies of a 64-row tile. "Row" layout (the
-// forward's K): LDS row r holds tile row bwd_perm(r), piece slot ^ (r % kNch). "Transposable"
-// layout (the forward's V): LDS row r holds tile row r, piece slot ^ 4 (r % (kNch / 4)).
+// 16-byte piece swizzle of LDS row r, for tiles the backward kernels read both ways: as rows
+// (ds_read_b128, 16 consecutive rows, one piece: the swizzle is a bijection on each aligned block
+// of 16 rows, and on each half of such a block taken in bwd_perm order it is distinct modulo 8)
+// and transposed (ds_read_b64_tr_b16, a 16-lane group reading two adjacent pieces of 4
+// consecutive rows: swizzle / 2 is distinct over each aligned group of 4 rows, and modulo 4 over
+// each aligned pair). So neither read shares a bank within a pass, whether the LDS serves 128 or
+// 256 bytes a cycle. With x = r % 16 (bits x3 x2 x1 x0): d = 128 (16 pieces per row)
+// (x3, x1, x0, x2 ^ x3); d = 64 (8 pieces; two rows share 256 bytes) (x0 ^ x1 ^ x3, x0 ^ x2, x1).
+template <int D>
+__device__ __forceinline__ int bwd_swz(int r) {
+  const int x0 = r & 1, x1 = (r >> 1) & 1, x2 = (r >> 2) & 1, x3 = (r >> 3) & 1;
+  if (D == 128) return (x3 << 3) | (x1 << 2) | (x0 << 1) | (x2 ^ x3);
+  return ((x0 ^ x1 ^ x3) << 2) | ((x0 ^ x2) << 1) | x1;
+}
+
+// Per-lane byte offsets of the direct HBM -> LDS copies of a 64-row tile (lane i of a KiB block
+// fills LDS row rb + i / kNch, slot i % kNch). Permuted rows (the dQ kernel's K): LDS row r holds
+// tile row bwd_perm(r); plain rows: LDS row r holds tile row r; piece slot ^ bwd_swz(r) in both.
 template <int D>
 __device__ __forceinline__ uint32_t bwd_off_row(int w, int it, int lane) {
   using C = BwdCfg<D>;
   const int row = (w * C::kKiBPerWave + it) * C::kRowsPerKiB + lane / C::kNch;
   const int slot = lane % C::kNch;
-  return (uint32_t)(bwd_perm(row) * C::kRowBytes + ((slot ^ (row % C::kNch)) << 4));
+  return (uint32_t)(bwd_perm(row) * C::kRowBytes + ((slot ^ bwd_swz<D>(row)) << 4));
 }
 template <int D>
 __device__ __forceinline__ uint32_t bwd_off_tr(int w, int it, int lane) {
   using C = BwdCfg<D>;
   const int row = (w * C::kKiBPerWave + it) * C::kRowsPerKiB + lane / C::kNch;
   const int slot = lane % C::kNch;
-  return (uint32_t)(row * C::kRowBytes + ((slot ^ (4 * (row % (C::kNch / 4)))) << 4));
+  return (uint32_t)(row * C::kRowBytes + ((slot ^ bwd_swz<D>(row)) << 4));
 }
 
 // ---- dQ. Wave w owns query rows q0 + 32w .. +31; per 64-key tile (K in the row layout, V in the
@@ -137,6 +169,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BackwardParams p) {
     lse2 = l == -kInf ? kInf : l * kLog2e;
     dlt = p.delta[qrow];
   }
+  // Wait for the register loads once and hide their origin, so the loop carries no vector-memory
+  // waits for them (such waits would also drain the tile copies in flight).
+  bwd_wait_vmcnt<0>();
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(qreg[ks]), "+v"(doreg[ks]));
+  asm volatile("" : "+v"(lse2), "+v"(dlt));
   const float c = p.scale * kLog2e;
 
   uint32_t koff[C::kKiBPerWave], voff[C::kKiBPerWave];
@@ -156,10 +194,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BackwardParams p) {
   };
 
   // A operand K rows (row layout): lane reads LDS row kb*32 + r32, piece 2 ks + g.
-  const int kx = r32 % C::kNch;
+  const int kx = bwd_swz<D>(r32);
   // A operand V rows in bwd_perm order from the transposable layout: LDS row kb*32 + vr.
   const int vr = bwd_perm(r32);
-  const int vsw = 4 * (vr % (C::kNch / 4));
+  const int vsw = bwd_swz<D>(vr);
   // A operand K^T (d x keys) by transposed reads of the row layout: in 16-lane group G
   // (gp = G%2), lane 4a+b addresses key 16u + 8g + 4rd + a, which sits in LDS row
   // 16u + 8rd + 4g + a, and d = db*32 + 16gp + 4b.
@@ -173,7 +211,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BackwardParams p) {
     for (int db = 0; db < D / 32; ++db) {
       const int r = 8 * rd + 4 * g + ta;
       const int piece = db * 4 + 2 * gp + (tb >> 1);
-      kt_off[rd][db] = r * C::kRowBytes + ((piece ^ (r % C::kNch)) << 4) + 8 * (tb & 1);
+      kt_off[rd][db] = r * C::kRowBytes + ((piece ^ bwd_swz<D>(r)) << 4) + 8 * (tb & 1);
     }
 
   f32x16 dq[D / 32];
@@ -243,9 +281,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BackwardParams p) {
     } else {
       bwd_wait_vmcnt<0>();
     }
-    __syncthreads();
+    bwd_barrier();
     step(stage_a, t * 64);
-    __syncthreads();
+    bwd_barrier();
     if (!more) break;
     if (t + 2 < ntiles) {
       issue(t + 2, stage_a);
@@ -253,9 +291,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BackwardParams p) {
     } else {
       bwd_wait_vmcnt<0>();
     }
-    __syncthreads();
+    bwd_barrier();
     step(stage_b, (t + 1) * 64);
-    __syncthreads();
+    bwd_barrier();
   }
   bwd_wait_vmcnt<0>();
 
@@ -273,19 +311,46 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BackwardParams p) {
   }
 }
 
-// ---- dK, dV. Wave w owns keys k0 + 32w .. +31; per 64-query tile (Q and dO in the transposable
-// layout, their lse2 and D in LDS): S = Q K^T and dP = dO V^T (queries x keys, one key per lane,
-// rows read in bwd_perm order), P = 2^(c s - lse2), dS = P (dP - D), dV^T += dO^T P,
-// dK^T += Q^T dS.
+// ---- dK, dV, two waves per SIMD. A workgroup of 8 waves owns 128 keys; waves w and w + 4 (one
+// SIMD) share the 32-key block kb = w & 3 and split the four products of each 64-query tile:
+//   phase A   P wave (w < 4):   S = Q K^T, P = 2^(c s - lse2) (masked), P -> LDS as bf16;
+//             dS wave (w >= 4): dP = dO V^T, kept in registers;
+//   barrier
+//   phase B   P wave:           dV^T += dO^T P (P still in its registers);
+//             dS wave:          P <- LDS, dS = P (dP - D), dK^T += Q^T dS;
+//   barrier (after this wave's copies of the next tile have landed).
+// Neither wave recomputes S; in each phase both issue 16 MFMAs per 32 keys, and the P wave's
+// exponentials (phase A) and the dS wave's dS (phase B) overlap the partner's matrix work on the
+// same SIMD. Rows are read in bwd_perm order, so the S accumulator of the P wave and the dP
+// accumulator of the dS wave hold the same (query, key) pairs entry by entry: P crosses over lane
+// for lane. Two stages (tile t, and tile t + 1 in flight) sit in the low 64 KiB of LDS so that every
+// stage address is a per-lane register plus an immediate; P and the lse/D rows lie above.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+struct BwdKvCfg {
+  static constexpr int kWaves = 8;
+  static constexpr int kNch = D / 8;
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = 64 * kRowBytes;            // a 64-row tile of Q or dO
+  static constexpr int kStageBytes = 2 * kTileBytes;           // Q tile, dO tile
+  static constexpr int kPBase = 2 * kStageBytes;
+  static constexpr int kPBytes = 4 * 4 * 64 * 16;              // 4 key blocks x 4 slots x 64 lanes x 16 B
+  static constexpr int kLsBase = kPBase + kPBytes;             // per stage: lse2[64], D[64]
+  static constexpr int kLdsBytes = kLsBase + 2 * 512;
+  static constexpr int kRowsPerKiB = 1024 / kRowBytes;
+  static constexpr int kKiBPerWave = kTileBytes / 1024 / kWaves;  // per tensor per tile
+  static_assert(kKiBPerWave * kWaves * 1024 == kTileBytes, "tile must split over the waves");
+  static_assert(kPBase <= 65536, "stages must sit within the LDS immediate-offset range");
+};
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BackwardParams p) {
-  using C = BwdCfg<D>;
-  constexpr int kStage = 2 * C::kTileBytes + 2 * 64 * 4;  // Q tile, dO tile, lse2[64], D[64]
-  __shared__ __attribute__((aligned(1024))) char stage_a[kStage];
-  __shared__ __attribute__((aligned(1024))) char stage_b[kStage];
+  using C = BwdKvCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb = w & 3;
+  const bool pwave = w < 4;
   const int r32 = lane & 31;
   const int g = lane >> 5;
   const int nkt = (p.Nk + 127) / 128;
@@ -294,7 +359,7 @@ void bwd_dkdv_kernel(BackwardParams p) {
   const int b = bh / p.H;
   const int k0 = kt * 128;
   const int L = seq_len(p.kv_seqlens, b, p.Nk);
-  const int kj = k0 + w * 32 + r32;  // this lane's key
+  const int kj = k0 + kb * 32 + r32;  // this lane's key
   // Query tiles that can see a key of this workgroup: from the first row at or after k0 when
   // causal, none when every key is past L.
   const int t0 = (p.causal && k0 < L) ? k0 / 64 : 0;
@@ -302,187 +367,248 @@ void bwd_dkdv_kernel(BackwardParams p) {
 
   const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + (size_t)bh * p.Nq * D;
   const uint16_t* dOg = static_cast<const uint16_t*>(p.dout) + (size_t)bh * p.Nq * D;
-  const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + (size_t)bh * p.Nk * D;
-  const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + (size_t)bh * p.Nk * D;
+  const uint16_t* KVg = static_cast<const uint16_t*>(pwave ? p.k : p.v) + (size_t)bh * p.Nk * D;
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, (uint32_t)p.Nq * C::kRowBytes);
   const __amdgpu_buffer_rsrc_t drs = make_rsrc(dOg, (uint32_t)p.Nq * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kg, (uint32_t)L * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vg, (uint32_t)L * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t kvrs = make_rsrc(KVg, (uint32_t)L * C::kRowBytes);
   const float* lse_bh = p.lse + (size_t)bh * p.Nq;
   const float* dl_bh = p.delta + (size_t)bh * p.Nq;
 
-  // B operands: lane (r32, g) holds K[key kj][16 ks + 8 g .. +8] and the same of V (keys past L
-  // read as zeros).
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  // B operands: lane (r32, g) holds K (P wave) or V (dS wave) of key kj, [16 ks + 8 g .. +8];
+  // keys past L read as zeros.
+  bf16x8 kv[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const uint32_t off = ((uint32_t)kj * D + ks * 16 + g * 8) * 2;
-    kreg[ks] = __builtin_bit_cast(bf16x8, buf_load16(krs, off));
-    vreg[ks] = __builtin_bit_cast(bf16x8, buf_load16(vrs, off));
-  }
+  for (int ks = 0; ks < D / 16; ++ks)
+    kv[ks] = __builtin_bit_cast(bf16x8, buf_load16(kvrs, ((uint32_t)kj * D + ks * 16 + g * 8) * 2));
+  // Wait for these loads once, then hide their origin: otherwise the loop's matrix instructions
+  // carry conservative vector-memory waits that also drain the next tile's copies issued just
+  // before them, serialising the prefetch.
+  bwd_wait_vmcnt<0>();
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(kv[ks]));
   const float c = p.scale * kLog2e;
 
+  // Copies of a query tile into a stage: LDS row r holds tile row r, 16-byte piece slot ^
+  // bwd_swz(r); wave w moves KiB blocks w*kKiBPerWave .. of each tensor.
   uint32_t toff[C::kKiBPerWave];
 #pragma unroll
-  for (int it = 0; it < C::kKiBPerWave; ++it) toff[it] = bwd_off_tr<D>(w, it, lane);
-  // Tile t: Q and dO rows by direct copies; lse2 and D of its 64 rows by wave 0 (registers, then
-  // LDS once they have landed).
-  float st_l = kInf, st_d = 0.0f;
-  auto issue = [&](int tile, char* stage) {
+  for (int it = 0; it < C::kKiBPerWave; ++it) {
+    const int row = (w * C::kKiBPerWave + it) * C::kRowsPerKiB + lane / C::kNch;
+    const int slot = lane % C::kNch;
+    toff[it] = (uint32_t)(row * C::kRowBytes + ((slot ^ bwd_swz<D>(row)) << 4));
+  }
+  float st_l = -kInf, st_d = 0.0f;  // wave 0: lse and D of the tile in flight, one row per lane
+  auto issue = [&](int tile, int stage) {
+    char* dst = smem + stage * C::kStageBytes;
     const uint32_t base = (uint32_t)tile * C::kTileBytes;
 #pragma unroll
     for (int it = 0; it < C::kKiBPerWave; ++it) {
-      char* blk = stage + (w * C::kKiBPerWave + it) * 1024;
+      char* blk = dst + (w * C::kKiBPerWave + it) * 1024;
       buf_load16_lds(qrs, blk, base + toff[it]);
       buf_load16_lds(drs, blk + C::kTileBytes, base + toff[it]);
     }
     if (w == 0) {
+      // Raw values only: converting them here would wait for the loads (and, counters draining
+      // in order, for the tile copies) at the start of the interval.
       const int qrow = tile * 64 + lane;
-      st_l = kInf;
+      st_l = -kInf;
       st_d = 0.0f;
       if (qrow < p.Nq) {
-        const float l = lse_bh[qrow];
-        st_l = l == -kInf ? kInf : l * kLog2e;
+        st_l = lse_bh[qrow];
         st_d = dl_bh[qrow];
       }
     }
   };
-  auto publish = [&](char* stage) {
+  auto publish = [&](int stage) {
     if (w == 0) {
-      float* ls = reinterpret_cast<float*>(stage + 2 * C::kTileBytes);
-      ls[lane] = st_l;
+      float* ls = reinterpret_cast<float*>(smem + C::kLsBase + stage * 512);
+      ls[lane] = st_l == -kInf ? kInf : st_l * kLog2e;  // +inf: rows past Nq or without keys
       ls[64 + lane] = st_d;
     }
   };
 
-  // A operands Q and dO rows in bwd_perm order from the transposable layout.
+  // Per-lane LDS offsets, computed once (the empty asm keeps them from being re-derived per use).
+  // Row operands (Q for the P wave, dO for the dS wave) in bwd_perm order: row qb*32 + bwd_perm(r32),
+  // piece (2 ks + g) ^ bwd_swz(row). Transposed operands (dO^T for the P wave, Q^T for the dS
+  // wave): in 16-lane group G (gp = G % 2), lane 4a+b addresses query 16u + 8g + 4rd + a,
+  // d = db*32 + 16gp + 4b. P crossing: key block kb, slot (qb, hh), lane. lse/D: query 8g + ...
   const int qr = bwd_perm(r32);
-  const int qsw = 4 * (qr % (C::kNch / 4));
-  // A operands Q^T and dO^T (d x queries) by transposed reads: lane 4a+b of 16-lane group G
-  // addresses query 16u + 8g + 4rd + a, d = db*32 + 16gp + 4b (the forward's V^T reads).
   const int li = lane & 15;
   const int ta = li >> 2, tb = li & 3;
   const int gp = (lane >> 4) & 1;
-  int tr_off[D / 32];
+  const int rt = pwave ? 0 : C::kTileBytes;  // tensor of the row operands within a stage
+  const int tt = pwave ? C::kTileBytes : 0;  // tensor of the transposed operands
+  uint32_t rofs[D / 16], tofs[2][D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    const int piece = db * 4 + 2 * gp + (tb >> 1);
-    const int sw = 4 * (ta % (C::kNch / 4));
-    tr_off[db] = (8 * g + ta) * C::kRowBytes + ((piece ^ sw) << 4) + 8 * (tb & 1);
+  for (int ks = 0; ks < D / 16; ++ks) {
+    rofs[ks] = (uint32_t)(rt + qr * C::kRowBytes + (((2 * ks + g) ^ bwd_swz<D>(qr)) << 4));
+    asm volatile("" : "+v"(rofs[ks]));
   }
-
-  f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
+  for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int piece = db * 4 + 2 * gp + (tb >> 1);
+      const int row = 8 * g + 4 * rd + ta;
+      tofs[rd][db] = (uint32_t)(tt + row * C::kRowBytes + ((piece ^ bwd_swz<D>(row)) << 4) + 8 * (tb & 1));
+      asm volatile("" : "+v"(tofs[rd][db]));
+    }
+  uint32_t pofs = (uint32_t)(C::kPBase + kb * 4 * 64 * 16 + lane * 16);
+  uint32_t lofs = (uint32_t)(C::kLsBase + 8 * g * 4);
+  asm volatile("" : "+v"(pofs), "+v"(lofs));
+
+  f32x16 acc[D / 32];  // dV^T (P wave) or dK^T (dS wave): entry e of block db is row kj, column
+#pragma unroll         // db*32 + 8(e/4) + 4g + e%4
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dk[db][e] = dv[db][e] = 0.0f;
+    for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
+  f32x16 xs[2];     // S (P wave) or dP (dS wave) of the tile's two 32-query blocks
+  bf16x8 pbv[2][2]; // the P wave's P operands of the tile
 
-  // One 32-query block at a time: S and dP of the block, then its P and dS, then its two 16-query
-  // steps of dV^T and dK^T (keeps the live accumulators to those of one block).
-  auto step = [&](const char* stage, int qt0) {
-    const char* Qs = stage;
-    const char* dOs = stage + C::kTileBytes;
-    const float* ls = reinterpret_cast<const float*>(stage + 2 * C::kTileBytes);
+  constexpr int kNR = 2 * (D / 16);  // phase A products: block qb = m / (D/16), step ks = m % (D/16)
+  constexpr int kNT = 4 * (D / 32);  // phase B products: slot u = m / (D/32) (qb = u/2, hh = u%2), db
+  constexpr int kAhead = 3;
+
+  // Phase A on stage S (tile `tile`): the row products, then (P wave) P and its copy to LDS.
+  auto phase_a = [&](auto stage_tag, int tile) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_tag)::value;
+    auto fetch = [&](int m) -> bf16x8 __attribute__((always_inline)) {
+      const int qb = m / (D / 16), ks = m % (D / 16);
+      return *reinterpret_cast<const bf16x8*>(smem + (S * C::kStageBytes + qb * 32 * C::kRowBytes + (int)rofs[ks]));
+    };
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s, dp;
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
-      const char* qrow = Qs + (qb * 32 + qr) * C::kRowBytes;
-      const char* drow = dOs + (qb * 32 + qr) * C::kRowBytes;
+      for (int e = 0; e < 16; ++e) xs[qb][e] = 0.0f;
+    bf16x8 op[kNR];
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const int pc = ((2 * ks + g) ^ qsw) << 4;
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qrow + pc);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(drow + pc);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[ks], dp, 0, 0, 0);
-      }
-      // Entry e is query qt0 + qb*32 + 16(e/8) + 8g + e%8 against this lane's key kj.
-      bf16x8 pb[2], dsb[2];
+    for (int m = 0; m < kAhead; ++m) op[m] = fetch(m);
+#pragma unroll
+    for (int m = 0; m < kNR; ++m) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (m + kAhead < kNR) op[m + kAhead] = fetch(m + kAhead);
+      const int qb = m / (D / 16), ks = m % (D / 16);
+      xs[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], kv[ks], xs[qb], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (!pwave) return;
+    // Entry e of block qb is query tile*64 + qb*32 + 16(e/8) + 8g + e%8 against key kj.
+    const float* ls = reinterpret_cast<const float*>(smem + (S * 512 + (int)lofs));
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int ql = qb * 32 + 16 * hh + 8 * g;  // tile-local query of entry hh*8
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls + ql);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + ql + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(ls + 64 + ql);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(ls + 64 + ql + 4);
-        u32x4 xp, xs;
+        const int qo = qb * 32 + 16 * hh;  // + 8g (in lofs)
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls + qo);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + qo + 4);
+        u32x4 xo;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          float pv[2], dsv[2];
+        for (int t2 = 0; t2 < 4; ++t2) {
+          float pv[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const int j = 2 * t + u;  // 0..7
-            const int e = hh * 8 + j;
-            const int qq = qt0 + ql + j;
+            const int j = 2 * t2 + u;
+            const int qq = tile * 64 + qo + 8 * g + j;
             const float lq = j < 4 ? l0[j] : l1[j - 4];
-            const float dq = j < 4 ? d0[j] : d1[j - 4];
             const bool ok = kj < L && (!p.causal || kj <= qq);
-            pv[u] = ok ? fast_exp2(fmaf(s[e], c, -lq)) : 0.0f;
-            dsv[u] = pv[u] * (dp[e] - dq);
+            pv[u] = ok ? fast_exp2(fmaf(xs[qb][hh * 8 + j], c, -lq)) : 0.0f;
           }
-          xp[t] = pack_bf16(pv[0], pv[1]);
-          xs[t] = pack_bf16(dsv[0], dsv[1]);
+          xo[t2] = pack_bf16(pv[0], pv[1]);
         }
-        pb[hh] = __builtin_bit_cast(bf16x8, xp);
-        dsb[hh] = __builtin_bit_cast(bf16x8, xs);
+        pbv[qb][hh] = __builtin_bit_cast(bf16x8, xo);
+        *reinterpret_cast<u32x4*>(smem + ((qb * 2 + hh) * 64 * 16 + (int)pofs)) = xo;
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-query steps.
+  };
+
+  // Phase B on stage S: (dS wave) P from LDS and dS; then the transposed products into acc.
+  auto phase_b = [&](auto stage_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_tag)::value;
+    auto fetch = [&](int m) -> bf16x8 __attribute__((always_inline)) {
+      const int u = m / (D / 32), db = m % (D / 32);
+      const int o = S * C::kStageBytes + u * 16 * C::kRowBytes;
+      const s16x4 a8[2] = {lds_read_tr16(smem + (o + (int)tofs[0][db])), lds_read_tr16(smem + (o + (int)tofs[1][db]))};
+      return __builtin_bit_cast(bf16x8, a8);
+    };
+    bf16x8 op[kNT];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+    for (int m = 0; m < kAhead; ++m) op[m] = fetch(m);
+    bf16x8 bop[2][2];
+    if (pwave) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int o = (qb * 2 + hh) * 16 * C::kRowBytes + tr_off[db];
-          const s16x4 da8[2] = {lds_read_tr16(dOs + o), lds_read_tr16(dOs + o + 4 * C::kRowBytes)};
-          const s16x4 qa8[2] = {lds_read_tr16(Qs + o), lds_read_tr16(Qs + o + 4 * C::kRowBytes)};
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, da8), pb[hh], dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa8), dsb[hh], dk[db], 0, 0, 0);
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) bop[qb][hh] = pbv[qb][hh];
+    } else {
+      const float* ls = reinterpret_cast<const float*>(smem + (S * 512 + (int)lofs));
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int qo = qb * 32 + 16 * hh;
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(ls + 64 + qo);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(ls + 64 + qo + 4);
+          const u32x4 pin = *reinterpret_cast<const u32x4*>(smem + ((qb * 2 + hh) * 64 * 16 + (int)pofs));
+          u32x4 xo;
+#pragma unroll
+          for (int t2 = 0; t2 < 4; ++t2) {
+            const int j0 = 2 * t2, j1 = 2 * t2 + 1;
+            const float dq0 = j0 < 4 ? d0[j0] : d1[j0 - 4];
+            const float dq1 = j1 < 4 ? d0[j1] : d1[j1 - 4];
+            xo[t2] = pack_bf16(bf16_lo(pin[t2]) * (xs[qb][hh * 8 + j0] - dq0),
+                               bf16_hi(pin[t2]) * (xs[qb][hh * 8 + j1] - dq1));
+          }
+          bop[qb][hh] = __builtin_bit_cast(bf16x8, xo);
         }
     }
+#pragma unroll
+    for (int m = 0; m < kNT; ++m) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (m + kAhead < kNT) op[m + kAhead] = fetch(m + kAhead);
+      const int u = m / (D / 32), db = m % (D / 32);
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], bop[u >> 1][u & 1], acc[db], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Interval for tile t on stage S: copy tile t + 1 into the other stage, phase A, barrier,
+  // phase B, this wave's copies landed, barrier.
+  auto interval = [&](auto stage_tag, int t) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_tag)::value;
+    const bool more = t + 1 < tn;
+    if (more) issue(t + 1, 1 - S);
+    phase_a(stage_tag, t);
+    bwd_barrier();
+    phase_b(stage_tag);
+    if (more) {
+      bwd_wait_vmcnt<0>();
+      publish(1 - S);
+    }
+    bwd_barrier();
   };
 
   if (t0 < tn) {
-    issue(t0, stage_a);
+    issue(t0, 0);
     bwd_wait_vmcnt<0>();
-    publish(stage_a);
+    publish(0);
   }
+  __syncthreads();
   for (int t = t0; t < tn; t += 2) {
-    const bool more = t + 1 < tn;
-    if (more) issue(t + 1, stage_b);
-    __syncthreads();  // stage_a (tile t) complete and visible
-    step(stage_a, t * 64);
-    if (more) {
-      bwd_wait_vmcnt<0>();
-      publish(stage_b);
-    }
-    __syncthreads();  // stage_a free, stage_b (tile t+1) complete
-    if (!more) break;
-    const bool more2 = t + 2 < tn;
-    if (more2) issue(t + 2, stage_a);
-    step(stage_b, (t + 1) * 64);
-    if (more2) {
-      bwd_wait_vmcnt<0>();
-      publish(stage_a);
-    }
-    __syncthreads();
+    interval(std::integral_constant<int, 0>{}, t);
+    if (t + 1 >= tn) break;
+    interval(std::integral_constant<int, 1>{}, t + 1);
   }
   bwd_wait_vmcnt<0>();
 
-  // dK^T / dV^T entry e of block db (lane r32, g) is row kj, column db*32 + 8(e/4) + 4g + e%4.
   if (kj < p.Nk) {
-    uint16_t* dKg = static_cast<uint16_t*>(p.dk) + (size_t)bh * p.Nk * D + (size_t)kj * D;
-    uint16_t* dVg = static_cast<uint16_t*>(p.dv) + (size_t)bh * p.Nk * D + (size_t)kj * D;
+    uint16_t* outg = static_cast<uint16_t*>(pwave ? p.dv : p.dk) + (size_t)bh * p.Nk * D + (size_t)kj * D;
+    const float f = pwave ? 1.0f : p.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq) {
-        const u32x2 xk = {pack_bf16(dk[db][4 * jq] * p.scale, dk[db][4 * jq + 1] * p.scale),
-                          pack_bf16(dk[db][4 * jq + 2] * p.scale, dk[db][4 * jq + 3] * p.scale)};
-        const u32x2 xv = {pack_bf16(dv[db][4 * jq], dv[db][4 * jq + 1]),
-                          pack_bf16(dv[db][4 * jq + 2], dv[db][4 * jq + 3])};
-        *reinterpret_cast<u32x2*>(dKg + db * 32 + 8 * jq + 4 * g) = xk;
-        *reinterpret_cast<u32x2*>(dVg + db * 32 + 8 * jq + 4 * g) = xv;
+        const u32x2 x = {pack_bf16(acc[db][4 * jq] * f, acc[db][4 * jq + 1] * f),
+                         pack_bf16(acc[db][4 * jq + 2] * f, acc[db][4 * jq + 3] * f)};
+        *reinterpret_cast<u32x2*>(outg + db * 32 + 8 * jq + 4 * g) = x;
       }
   }
 }
@@ -501,8 +627,8 @@ hipError_t launch_backward(const BackwardParams& p, int d, hipStream_t stream) {
   }
   if (p.Nk > 0) {
     const dim3 g2((unsigned)(bh * ((p.Nk + 127) / 128)));
-    if (d == 64) hipLaunchKernelGGL(bwd_dkdv_kernel<64>, g2, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(bwd_dkdv_kernel<128>, g2, dim3(256), 0, stream, p);
+    if (d == 64) hipLaunchKernelGGL(bwd_dkdv_kernel<64>, g2, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL(bwd_dkdv_kernel<128>, g2, dim3(512), 0, stream, p);
   }
   return hipGetLastError();
 }
