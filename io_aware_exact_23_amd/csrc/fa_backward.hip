@@ -132,9 +132,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BackwardParams p) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31;
   const int g = lane >> 5;
+  // Workgroups in order of decreasing work: under causal masking the last query tiles of every
+  // head first (the head index runs fastest), so the heaviest tiles never start last.
   const int nqt = (p.Nq + 127) / 128;
-  const int bh = blockIdx.x / nqt;
-  const int qt = blockIdx.x - bh * nqt;
+  const int nbh = p.B * p.H;
+  const int qr_ = blockIdx.x / nbh;
+  const int bh = blockIdx.x - qr_ * nbh;
+  const int qt = p.causal ? nqt - 1 - qr_ : qr_;
   const int b = bh / p.H;
   const int q0 = qt * 128;
   const int L = seq_len(p.kv_seqlens, b, p.Nk);
@@ -353,9 +357,12 @@ void bwd_dkdv_kernel(BackwardParams p) {
   const bool pwave = w < 4;
   const int r32 = lane & 31;
   const int g = lane >> 5;
+  // Workgroups in order of decreasing work: under causal masking the first key tiles of every head
+  // first (the head index runs fastest), so the heaviest tiles never start last.
   const int nkt = (p.Nk + 127) / 128;
-  const int bh = blockIdx.x / nkt;
-  const int kt = blockIdx.x - bh * nkt;
+  const int nbh = p.B * p.H;
+  const int kt = blockIdx.x / nbh;
+  const int bh = blockIdx.x - kt * nbh;
   const int b = bh / p.H;
   const int k0 = kt * 128;
   const int L = seq_len(p.kv_seqlens, b, p.Nk);
@@ -576,7 +583,11 @@ void bwd_dkdv_kernel(BackwardParams p) {
     constexpr int S = decltype(stage_tag)::value;
     const bool more = t + 1 < tn;
     if (more) issue(t + 1, 1 - S);
+    // The P wave runs phase A at raised priority, so its matrix work issues first and its
+    // exponentials then overlap the partner's matrix work.
+    if (pwave) __builtin_amdgcn_s_setprio(1);
     phase_a(stage_tag, t);
+    __builtin_amdgcn_s_setprio(0);
     bwd_barrier();
     phase_b(stage_tag);
     if (more) {
