@@ -9,8 +9,9 @@
 //   dS_ij = P_ij (dP_ij - D_i),  dQ_i += scale dS_ij k_j,  dK_j += scale dS_ij q_i.
 // Three kernels:
 //   bwd_delta_kernel  D_i = dO_i . O_i for every query row (fp32);
-//   bwd_dq_kernel     one workgroup of 4 waves per 128 query rows, K/V tiles through LDS as in
-//                     the forward kernel: S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T;
+//   bwd_dq_kernel     one workgroup of 8 waves per 128 query rows, K/V tiles through LDS; per
+//                     SIMD one wave computes S^T = K Q^T and P^T, its partner dP^T = V dO^T,
+//                     then both dS^T and half each of dQ^T += K^T dS^T;
 //   bwd_dkdv_kernel   one workgroup of 8 waves per 128 keys, Q/dO tiles through LDS; per SIMD
 //                     one wave computes S = Q K^T, P and dV^T += dO^T P, its partner dP = dO V^T,
 //                     then (taking P through LDS) dS and dK^T += Q^T dS.
@@ -120,16 +121,43 @@ __device__ __forceinline__ uint32_t bwd_off_tr(int w, int it, int lane) {
   return (uint32_t)(row * C::kRowBytes + ((slot ^ bwd_swz<D>(row)) << 4));
 }
 
-// ---- dQ. Wave w owns query rows q0 + 32w .. +31; per 64-key tile (K in the row layout, V in the
-// transposable layout): S^T = K Q^T and dP^T = V dO^T (keys x queries, one query per lane),
-// P^T = 2^(c s - lse2), dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
+// ---- dQ, two waves per SIMD. A workgroup of 8 waves owns 128 query rows; waves w and w + 4 (one
+// SIMD) share the 32-row block qb = w & 3, with one query per lane in both. Per 64-key tile (K with
+// rows in bwd_perm order and V, both in stages of LDS):
+//   phase A   S wave (w < 4):   S^T = K Q^T, P^T = 2^(c s - lse2) (masked) -> LDS as bf16;
+//             dP wave (w >= 4): dP^T = V dO^T, (dP^T - D) -> LDS as bf16;
+//   barrier
+//   phase B   both: dS^T = P^T (dP^T - D) from their own value and the partner's, then
+//             dQ^T += K^T dS^T for half of the head dimension each (S wave the low half);
+//   barrier (after this wave's copies of the next tile have landed).
+// 24 MFMAs per wave and tile, none recomputed, and the S wave's exponentials overlap the dP wave's
+// matrix work on the same SIMD.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BackwardParams p) {
-  using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char stage_a[2 * C::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char stage_b[2 * C::kTileBytes];
+struct BwdQCfg {
+  static constexpr int kWaves = 8;
+  static constexpr int kNch = D / 8;
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = 64 * kRowBytes;            // a 64-key tile of K or V
+  static constexpr int kStageBytes = 2 * kTileBytes;           // K tile, V tile
+  static constexpr int kXBase = 2 * kStageBytes;
+  static constexpr int kXBytes = 4 * 2 * 4 * 64 * 16;          // 4 pairs x 2 values x 4 slots x 64 lanes x 16 B
+  static constexpr int kLdsBytes = kXBase + kXBytes;
+  static constexpr int kRowsPerKiB = 1024 / kRowBytes;
+  static constexpr int kKiBPerWave = kTileBytes / 1024 / kWaves;  // per tensor per tile
+  static constexpr int kHalf = D / 64;                         // 32-d blocks of dQ per wave
+  static_assert(kKiBPerWave * kWaves * 1024 == kTileBytes, "tile must split over the waves");
+  static_assert(kXBase <= 65536, "stages must sit within the LDS immediate-offset range");
+};
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BackwardParams p) {
+  using C = BwdQCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qb = w & 3;
+  const bool swave = w < 4;
   const int r32 = lane & 31;
   const int g = lane >> 5;
   // Workgroups in order of decreasing work: under causal masking the last query tiles of every
@@ -146,171 +174,224 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BackwardParams p) {
   if (p.causal) kend = min(kend, min(q0 + 128, p.Nq));
   const int ntiles = kend > 0 ? (kend + 63) / 64 : 0;
 
-  const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + (size_t)bh * p.Nq * D;
-  const uint16_t* dOg = static_cast<const uint16_t*>(p.dout) + (size_t)bh * p.Nq * D;
+  const uint16_t* QDg = static_cast<const uint16_t*>(swave ? p.q : p.dout) + (size_t)bh * p.Nq * D;
   const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + (size_t)bh * p.Nk * D;
   const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + (size_t)bh * p.Nk * D;
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, (uint32_t)p.Nq * C::kRowBytes);
-  const __amdgpu_buffer_rsrc_t drs = make_rsrc(dOg, (uint32_t)p.Nq * C::kRowBytes);
+  const __amdgpu_buffer_rsrc_t qdrs = make_rsrc(QDg, (uint32_t)p.Nq * C::kRowBytes);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kg, (uint32_t)kend * C::kRowBytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vg, (uint32_t)kend * C::kRowBytes);
 
-  // B operands: lane (r32, g) holds Q[row r32][16 ks + 8 g .. +8] and the same of dO.
-  const int qw0 = q0 + w * 32;
-  const int qi = qw0 + r32;
-  bf16x8 qreg[D / 16], doreg[D / 16];
+  // B operands: lane (r32, g) holds Q (S wave) or dO (dP wave) of query qi, [16 ks + 8 g .. +8].
+  const int qi = q0 + qb * 32 + r32;
+  bf16x8 qd[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const uint32_t off = ((uint32_t)qi * D + ks * 16 + g * 8) * 2;
-    qreg[ks] = __builtin_bit_cast(bf16x8, buf_load16(qrs, off));
-    doreg[ks] = __builtin_bit_cast(bf16x8, buf_load16(drs, off));
-  }
-  // This lane's query: base-2 logsumexp (+inf for rows past Nq or without keys: P = 0) and D.
-  const size_t qrow = (size_t)bh * p.Nq + qi;
-  float lse2 = kInf, dlt = 0.0f;
+  for (int ks = 0; ks < D / 16; ++ks)
+    qd[ks] = __builtin_bit_cast(bf16x8, buf_load16(qdrs, ((uint32_t)qi * D + ks * 16 + g * 8) * 2));
+  // The S wave needs this query's base-2 logsumexp (+inf for rows past Nq or without keys: P = 0),
+  // the dP wave its D.
+  float lsd = swave ? kInf : 0.0f;
   if (qi < p.Nq) {
-    const float l = p.lse[qrow];
-    lse2 = l == -kInf ? kInf : l * kLog2e;
-    dlt = p.delta[qrow];
+    const size_t qrow = (size_t)bh * p.Nq + qi;
+    if (swave) {
+      const float l = p.lse[qrow];
+      lsd = l == -kInf ? kInf : l * kLog2e;
+    } else {
+      lsd = p.delta[qrow];
+    }
   }
   // Wait for the register loads once and hide their origin, so the loop carries no vector-memory
   // waits for them (such waits would also drain the tile copies in flight).
   bwd_wait_vmcnt<0>();
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(qreg[ks]), "+v"(doreg[ks]));
-  asm volatile("" : "+v"(lse2), "+v"(dlt));
+  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(qd[ks]));
+  asm volatile("" : "+v"(lsd));
   const float c = p.scale * kLog2e;
 
+  // Tile copies: K rows permuted (LDS row r holds key bwd_perm(r)), V rows plain, pieces slot ^
+  // bwd_swz(r); wave w moves KiB blocks w*kKiBPerWave .. of each tensor.
   uint32_t koff[C::kKiBPerWave], voff[C::kKiBPerWave];
 #pragma unroll
   for (int it = 0; it < C::kKiBPerWave; ++it) {
-    koff[it] = bwd_off_row<D>(w, it, lane);
-    voff[it] = bwd_off_tr<D>(w, it, lane);
+    const int row = (w * C::kKiBPerWave + it) * C::kRowsPerKiB + lane / C::kNch;
+    const int slot = lane % C::kNch;
+    koff[it] = (uint32_t)(bwd_perm(row) * C::kRowBytes + ((slot ^ bwd_swz<D>(row)) << 4));
+    voff[it] = (uint32_t)(row * C::kRowBytes + ((slot ^ bwd_swz<D>(row)) << 4));
   }
-  auto issue = [&](int tile, char* stage) {
+  auto issue = [&](int tile, int stage) {
+    char* dst = smem + stage * C::kStageBytes;
     const uint32_t base = (uint32_t)tile * C::kTileBytes;
 #pragma unroll
     for (int it = 0; it < C::kKiBPerWave; ++it) {
-      char* blk = stage + (w * C::kKiBPerWave + it) * 1024;
+      char* blk = dst + (w * C::kKiBPerWave + it) * 1024;
       buf_load16_lds(krs, blk, base + koff[it]);
       buf_load16_lds(vrs, blk + C::kTileBytes, base + voff[it]);
     }
   };
 
-  // A operand K rows (row layout): lane reads LDS row kb*32 + r32, piece 2 ks + g.
-  const int kx = bwd_swz<D>(r32);
-  // A operand V rows in bwd_perm order from the transposable layout: LDS row kb*32 + vr.
-  const int vr = bwd_perm(r32);
-  const int vsw = bwd_swz<D>(vr);
-  // A operand K^T (d x keys) by transposed reads of the row layout: in 16-lane group G
-  // (gp = G%2), lane 4a+b addresses key 16u + 8g + 4rd + a, which sits in LDS row
-  // 16u + 8rd + 4g + a, and d = db*32 + 16gp + 4b.
+  // Per-lane LDS offsets. Row operands: K (S wave) LDS row kb*32 + r32, V (dP wave) LDS row
+  // kb*32 + bwd_perm(r32) (its keys in the S wave's order), piece (2 ks + g) ^ bwd_swz(row).
+  // K^T operands (both): in 16-lane group G (gp = G % 2), lane 4a+b addresses key
+  // 16u + 8g + 4rd + a, which sits in LDS row 16u + 8rd + 4g + a, and d = db*32 + 16gp + 4b for
+  // this wave's half of the blocks db. Exchange: own and partner slots of pair qb.
   const int li = lane & 15;
   const int ta = li >> 2, tb = li & 3;
   const int gp = (lane >> 4) & 1;
-  int kt_off[2][D / 32];
+  const int rrow = swave ? r32 : bwd_perm(r32);
+  uint32_t rofs[D / 16], kt[2][C::kHalf];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    rofs[ks] = (uint32_t)((swave ? 0 : C::kTileBytes) + rrow * C::kRowBytes + (((2 * ks + g) ^ bwd_swz<D>(rrow)) << 4));
+    asm volatile("" : "+v"(rofs[ks]));
+  }
+  const int db0 = swave ? 0 : C::kHalf;
 #pragma unroll
   for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int j = 0; j < C::kHalf; ++j) {
       const int r = 8 * rd + 4 * g + ta;
-      const int piece = db * 4 + 2 * gp + (tb >> 1);
-      kt_off[rd][db] = r * C::kRowBytes + ((piece ^ bwd_swz<D>(r)) << 4) + 8 * (tb & 1);
+      const int piece = (db0 + j) * 4 + 2 * gp + (tb >> 1);
+      kt[rd][j] = (uint32_t)(r * C::kRowBytes + ((piece ^ bwd_swz<D>(r)) << 4) + 8 * (tb & 1));
+      asm volatile("" : "+v"(kt[rd][j]));
     }
+  uint32_t xown = (uint32_t)(C::kXBase + qb * 8192 + (swave ? 0 : 4096) + lane * 16);
+  uint32_t xoth = (uint32_t)(C::kXBase + qb * 8192 + (swave ? 4096 : 0) + lane * 16);
+  asm volatile("" : "+v"(xown), "+v"(xoth));
 
-  f32x16 dq[D / 32];
+  f32x16 acc[C::kHalf];  // dQ^T: entry e of block j is dQ[qi][(db0 + j)*32 + 8(e/4) + 4g + e%4]
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int j = 0; j < C::kHalf; ++j)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dq[db][e] = 0.0f;
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+  f32x16 xs[2];  // P^T (S wave) or dP^T - D (dP wave) of the tile's two 32-key blocks
 
-  auto step = [&](const char* stage, int k0) {
-    const char* Ks = stage;
-    const char* Vs = stage + C::kTileBytes;
-    f32x16 s[2], dp[2];
+  constexpr int kNR = 2 * (D / 16);    // phase A: key block kb = m & 1, step ks = m >> 1
+  constexpr int kNT = 4 * C::kHalf;    // phase B: 16-key step u = m / kHalf, block j = m % kHalf
+  constexpr int kAhead = 3;
+
+  auto phase_a = [&](auto stage_tag, int k0) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_tag)::value;
+    auto fetch = [&](int m) -> bf16x8 __attribute__((always_inline)) {
+      const int kb = m & 1, ks = m >> 1;
+      return *reinterpret_cast<const bf16x8*>(smem + (S * C::kStageBytes + kb * 32 * C::kRowBytes + (int)rofs[ks]));
+    };
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = dp[kb][e] = 0.0f;
-      const char* krow = Ks + (kb * 32 + r32) * C::kRowBytes;
-      const char* vrow = Vs + (kb * 32 + vr) * C::kRowBytes;
+      for (int e = 0; e < 16; ++e) xs[kb][e] = 0.0f;
+    bf16x8 op[kNR];
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + (((2 * ks + g) ^ kx) << 4));
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + (((2 * ks + g) ^ vsw) << 4));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, doreg[ks], dp[kb], 0, 0, 0);
-      }
+    for (int m = 0; m < kAhead; ++m) op[m] = fetch(m);
+#pragma unroll
+    for (int m = 0; m < kNR; ++m) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (m + kAhead < kNR) op[m + kAhead] = fetch(m + kAhead);
+      xs[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], qd[m >> 1], xs[m & 1], 0, 0, 0);
     }
-    // Entry e of block kb is key k0 + kb*32 + 16(e/8) + 8g + e%8 of this lane's query qi.
+    __builtin_amdgcn_sched_barrier(0);
+    // Entry e of block kb is key k0 + kb*32 + 16(e/8) + 8g + e%8 of this lane's query qi. The
+    // mask (keys past L, keys after the query when causal) matters only on tiles reaching past L
+    // or past the workgroup's first row: elsewhere one FMA and one exponential per score.
     const int rem = (p.causal ? min(L, qi + 1) : L) - (k0 + 8 * g);
+    const bool masked = k0 + 64 > L || (p.causal && k0 + 63 > q0);
+    auto values = [&](auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool kMask = decltype(mask_tag)::value;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          u32x4 xo;
+#pragma unroll
+          for (int t2 = 0; t2 < 4; ++t2) {
+            float v2[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int e = hh * 8 + 2 * t2 + u;
+              if (swave) {
+                const float e2 = fast_exp2(fmaf(xs[kb][e], c, -lsd));
+                if constexpr (kMask) v2[u] = (kb * 32 + 16 * hh + 2 * t2 + u < rem) ? e2 : 0.0f;
+                else v2[u] = e2;
+              } else {
+                v2[u] = xs[kb][e] - lsd;
+              }
+              xs[kb][e] = v2[u];
+            }
+            xo[t2] = pack_bf16(v2[0], v2[1]);
+          }
+          *reinterpret_cast<u32x4*>(smem + ((kb * 2 + hh) * 1024 + (int)xown)) = xo;
+        }
+    };
+    if (masked && swave) values(std::true_type{});
+    else values(std::false_type{});
+  };
+
+  auto phase_b = [&](auto stage_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_tag)::value;
+    auto fetch = [&](int m) -> bf16x8 __attribute__((always_inline)) {
+      const int u = m / C::kHalf, j = m % C::kHalf;
+      const int o = S * C::kStageBytes + u * 16 * C::kRowBytes;
+      const s16x4 a8[2] = {lds_read_tr16(smem + (o + (int)kt[0][j])), lds_read_tr16(smem + (o + (int)kt[1][j]))};
+      return __builtin_bit_cast(bf16x8, a8);
+    };
+    bf16x8 op[kNT];
+#pragma unroll
+    for (int m = 0; m < kAhead; ++m) op[m] = fetch(m);
+    // dS^T = own value times the partner's (P^T times dP^T - D), as bf16 B operands.
     bf16x8 dsk[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        u32x4 x;
+        const u32x4 oth = *reinterpret_cast<const u32x4*>(smem + ((kb * 2 + hh) * 1024 + (int)xoth));
+        u32x4 xo;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          float ds2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int e = hh * 8 + 2 * t + u;
-            const bool ok = kb * 32 + 16 * hh + 2 * t + u < rem;
-            const float pr = ok ? fast_exp2(fmaf(s[kb][e], c, -lse2)) : 0.0f;
-            ds2[u] = pr * (dp[kb][e] - dlt);
-          }
-          x[t] = pack_bf16(ds2[0], ds2[1]);
-        }
-        dsk[kb][hh] = __builtin_bit_cast(bf16x8, x);
+        for (int t2 = 0; t2 < 4; ++t2)
+          xo[t2] = pack_bf16(xs[kb][hh * 8 + 2 * t2] * bf16_lo(oth[t2]), xs[kb][hh * 8 + 2 * t2 + 1] * bf16_hi(oth[t2]));
+        dsk[kb][hh] = __builtin_bit_cast(bf16x8, xo);
       }
-    // dQ^T += K^T dS^T over the tile's four 16-key steps.
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const char* base = Ks + u * 16 * C::kRowBytes;
-        const s16x4 a8[2] = {lds_read_tr16(base + kt_off[0][db]), lds_read_tr16(base + kt_off[1][db])};
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), dsk[u >> 1][u & 1],
-                                                        dq[db], 0, 0, 0);
-      }
+    for (int m = 0; m < kNT; ++m) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (m + kAhead < kNT) op[m + kAhead] = fetch(m + kAhead);
+      const int u = m / C::kHalf, j = m % C::kHalf;
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], dsk[u >> 1][u & 1], acc[j], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  if (ntiles > 0) issue(0, stage_a);
-  for (int t = 0; t < ntiles; t += 2) {
+  auto interval = [&](auto stage_tag, int t) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_tag)::value;
     const bool more = t + 1 < ntiles;
-    if (more) {
-      issue(t + 1, stage_b);
-      bwd_wait_vmcnt<2 * C::kKiBPerWave>();
-    } else {
-      bwd_wait_vmcnt<0>();
-    }
+    if (more) issue(t + 1, 1 - S);
+    if (swave) __builtin_amdgcn_s_setprio(1);
+    phase_a(stage_tag, t * 64);
+    __builtin_amdgcn_s_setprio(0);
     bwd_barrier();
-    step(stage_a, t * 64);
+    phase_b(stage_tag);
+    if (more) bwd_wait_vmcnt<0>();
     bwd_barrier();
-    if (!more) break;
-    if (t + 2 < ntiles) {
-      issue(t + 2, stage_a);
-      bwd_wait_vmcnt<2 * C::kKiBPerWave>();
-    } else {
-      bwd_wait_vmcnt<0>();
-    }
-    bwd_barrier();
-    step(stage_b, (t + 1) * 64);
-    bwd_barrier();
+  };
+
+  if (ntiles > 0) {
+    issue(0, 0);
+    bwd_wait_vmcnt<0>();
+  }
+  bwd_barrier();
+  for (int t = 0; t < ntiles; t += 2) {
+    interval(std::integral_constant<int, 0>{}, t);
+    if (t + 1 >= ntiles) break;
+    interval(std::integral_constant<int, 1>{}, t + 1);
   }
   bwd_wait_vmcnt<0>();
 
-  // dQ^T entry e of block db (lane r32, g) is dQ[qi][db*32 + 8(e/4) + 4g + e%4].
   if (qi < p.Nq) {
     uint16_t* dQg = static_cast<uint16_t*>(p.dq) + (size_t)bh * p.Nq * D + (size_t)qi * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int j = 0; j < C::kHalf; ++j)
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq) {
-        const u32x2 x = {pack_bf16(dq[db][4 * jq] * p.scale, dq[db][4 * jq + 1] * p.scale),
-                         pack_bf16(dq[db][4 * jq + 2] * p.scale, dq[db][4 * jq + 3] * p.scale)};
-        *reinterpret_cast<u32x2*>(dQg + db * 32 + 8 * jq + 4 * g) = x;
+        const u32x2 x = {pack_bf16(acc[j][4 * jq] * p.scale, acc[j][4 * jq + 1] * p.scale),
+                         pack_bf16(acc[j][4 * jq + 2] * p.scale, acc[j][4 * jq + 3] * p.scale)};
+        *reinterpret_cast<u32x2*>(dQg + (db0 + j) * 32 + 8 * jq + 4 * g) = x;
       }
   }
 }
@@ -471,6 +552,7 @@ void bwd_dkdv_kernel(BackwardParams p) {
     for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
   f32x16 xs[2];     // S (P wave) or dP (dS wave) of the tile's two 32-query blocks
   bf16x8 pbv[2][2]; // the P wave's P operands of the tile
+  f32x4 lq[2][2][2];  // lse2 (P wave) or D (dS wave) of this lane's 8 queries per (qb, hh)
 
   constexpr int kNR = 2 * (D / 16);  // phase A products: block qb = m / (D/16), step ks = m % (D/16)
   constexpr int kNT = 4 * (D / 32);  // phase B products: slot u = m / (D/32) (qb = u/2, hh = u%2), db
@@ -490,6 +572,18 @@ void bwd_dkdv_kernel(BackwardParams p) {
     bf16x8 op[kNR];
 #pragma unroll
     for (int m = 0; m < kAhead; ++m) op[m] = fetch(m);
+    // This lane's lse2 (P wave, for P) or D (dS wave, for dS in phase B), read ahead of the matrix
+    // work so that their latency is hidden behind it.
+    {
+      const float* lsr = reinterpret_cast<const float*>(smem + (S * 512 + (int)lofs)) + (pwave ? 0 : 64);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          lq[qb][hh][0] = *reinterpret_cast<const f32x4*>(lsr + qb * 32 + 16 * hh);
+          lq[qb][hh][1] = *reinterpret_cast<const f32x4*>(lsr + qb * 32 + 16 * hh + 4);
+        }
+    }
 #pragma unroll
     for (int m = 0; m < kNR; ++m) {
       __builtin_amdgcn_sched_barrier(0);
@@ -499,32 +593,44 @@ void bwd_dkdv_kernel(BackwardParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
     if (!pwave) return;
-    // Entry e of block qb is query tile*64 + qb*32 + 16(e/8) + 8g + e%8 against key kj.
-    const float* ls = reinterpret_cast<const float*>(smem + (S * 512 + (int)lofs));
+    // Entry e of block qb is query tile*64 + qb*32 + 16(e/8) + 8g + e%8 against key kj. The mask
+    // (keys past L, keys after the query when causal) matters only on the workgroup's diagonal
+    // tiles and in a ragged last key block: elsewhere one FMA and one exponential per score.
+    const bool masked = k0 + 128 > L || (p.causal && tile * 64 < k0 + 128);
+    auto p_values = [&](auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool kMask = decltype(mask_tag)::value;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int qo = qb * 32 + 16 * hh;  // + 8g (in lofs)
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls + qo);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + qo + 4);
-        u32x4 xo;
+        for (int hh = 0; hh < 2; ++hh) {
+          const int qo = qb * 32 + 16 * hh;  // + 8g (in lofs)
+          const f32x4 l0 = lq[qb][hh][0];
+          const f32x4 l1 = lq[qb][hh][1];
+          u32x4 xo;
 #pragma unroll
-        for (int t2 = 0; t2 < 4; ++t2) {
-          float pv[2];
+          for (int t2 = 0; t2 < 4; ++t2) {
+            float pv[2];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int j = 2 * t2 + u;
-            const int qq = tile * 64 + qo + 8 * g + j;
-            const float lq = j < 4 ? l0[j] : l1[j - 4];
-            const bool ok = kj < L && (!p.causal || kj <= qq);
-            pv[u] = ok ? fast_exp2(fmaf(xs[qb][hh * 8 + j], c, -lq)) : 0.0f;
+            for (int u = 0; u < 2; ++u) {
+              const int j = 2 * t2 + u;
+              const float lq = j < 4 ? l0[j] : l1[j - 4];
+              const float e2 = fast_exp2(fmaf(xs[qb][hh * 8 + j], c, -lq));
+              if constexpr (kMask) {
+                const int qq = tile * 64 + qo + 8 * g + j;
+                const bool ok = kj < L && (!p.causal || kj <= qq);
+                pv[u] = ok ? e2 : 0.0f;
+              } else {
+                pv[u] = e2;
+              }
+            }
+            xo[t2] = pack_bf16(pv[0], pv[1]);
           }
-          xo[t2] = pack_bf16(pv[0], pv[1]);
+          pbv[qb][hh] = __builtin_bit_cast(bf16x8, xo);
+          *reinterpret_cast<u32x4*>(smem + ((qb * 2 + hh) * 64 * 16 + (int)pofs)) = xo;
         }
-        pbv[qb][hh] = __builtin_bit_cast(bf16x8, xo);
-        *reinterpret_cast<u32x4*>(smem + ((qb * 2 + hh) * 64 * 16 + (int)pofs)) = xo;
-      }
+    };
+    if (masked) p_values(std::true_type{});
+    else p_values(std::false_type{});
   };
 
   // Phase B on stage S: (dS wave) P from LDS and dS; then the transposed products into acc.
@@ -546,14 +652,12 @@ void bwd_dkdv_kernel(BackwardParams p) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) bop[qb][hh] = pbv[qb][hh];
     } else {
-      const float* ls = reinterpret_cast<const float*>(smem + (S * 512 + (int)lofs));
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int qo = qb * 32 + 16 * hh;
-          const f32x4 d0 = *reinterpret_cast<const f32x4*>(ls + 64 + qo);
-          const f32x4 d1 = *reinterpret_cast<const f32x4*>(ls + 64 + qo + 4);
+          const f32x4 d0 = lq[qb][hh][0];
+          const f32x4 d1 = lq[qb][hh][1];
           const u32x4 pin = *reinterpret_cast<const u32x4*>(smem + ((qb * 2 + hh) * 64 * 16 + (int)pofs));
           u32x4 xo;
 #pragma unroll
@@ -633,8 +737,8 @@ hipError_t launch_backward(const BackwardParams& p, int d, hipStream_t stream) {
     if (d == 64) hipLaunchKernelGGL(bwd_delta_kernel<64>, g0, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL(bwd_delta_kernel<128>, g0, dim3(256), 0, stream, p);
     const dim3 g1((unsigned)(bh * ((p.Nq + 127) / 128)));
-    if (d == 64) hipLaunchKernelGGL(bwd_dq_kernel<64>, g1, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(bwd_dq_kernel<128>, g1, dim3(256), 0, stream, p);
+    if (d == 64) hipLaunchKernelGGL(bwd_dq_kernel<64>, g1, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL(bwd_dq_kernel<128>, g1, dim3(512), 0, stream, p);
   }
   if (p.Nk > 0) {
     const dim3 g2((unsigned)(bh * ((p.Nk + 127) / 128)));
