@@ -293,7 +293,10 @@ void bwd_dq_kernel(BackwardParams p) {
     // or past the workgroup's first row: elsewhere one FMA and one exponential per score.
     const int rem = (p.causal ? min(L, qi + 1) : L) - (k0 + 8 * g);
     const bool masked = k0 + 64 > L || (p.causal && k0 + 63 > q0);
-    auto values = [&](auto mask_tag) __attribute__((always_inline)) {
+    // One code path per role and mask case (a role test inside the loop would be if-converted,
+    // making every wave compute both roles' values).
+    auto values = [&](auto role_tag, auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool kS = decltype(role_tag)::value;
       constexpr bool kMask = decltype(mask_tag)::value;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -306,7 +309,7 @@ void bwd_dq_kernel(BackwardParams p) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
               const int e = hh * 8 + 2 * t2 + u;
-              if (swave) {
+              if constexpr (kS) {
                 const float e2 = fast_exp2(fmaf(xs[kb][e], c, -lsd));
                 if constexpr (kMask) v2[u] = (kb * 32 + 16 * hh + 2 * t2 + u < rem) ? e2 : 0.0f;
                 else v2[u] = e2;
@@ -320,8 +323,12 @@ void bwd_dq_kernel(BackwardParams p) {
           *reinterpret_cast<u32x4*>(smem + ((kb * 2 + hh) * 1024 + (int)xown)) = xo;
         }
     };
-    if (masked && swave) values(std::true_type{});
-    else values(std::false_type{});
+    if (swave) {
+      if (masked) values(std::true_type{}, std::true_type{});
+      else values(std::true_type{}, std::false_type{});
+    } else {
+      values(std::false_type{}, std::false_type{});
+    }
   };
 
   auto phase_b = [&](auto stage_tag) __attribute__((always_inline)) {
