@@ -51,6 +51,8 @@ KERNEL_SOURCES = {
     "prefill_bf16_kernel": ["fa_prefill_bf16.hip", "fa_softmax.h"] + _COMMON,
     "decode_split_kernel": ["fa_decode.hip"] + _COMMON,
     "prefill_fp8_kernel": ["fa_prefill_fp8.hip"] + _COMMON,
+    "bwd_dq_kernel": ["fa_backward.hip"] + _COMMON,
+    "bwd_dkdv_kernel": ["fa_backward.hip"] + _COMMON,
 }
 PREFILL_WORKLOADS = ["gpt2s_causal_b8_h12_n1024_d64", "bertl_padded_b16_h16_n512_d64",
                      "long_causal_b2_h16_n16384_d128"]
