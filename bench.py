@@ -196,10 +196,17 @@ def bench_standard(fa, configs, inputs, torch, dev, steps, warmup, main_name):
         lens_np = None if lens is None else lens.cpu().numpy()
         nbytes = standard_bytes(w, lens_np)
         avg = float(np.mean(per_std))
+        # Forward rate of the tiled call: FLOPs counted as 4*B*H*Nq*Nk*d (halved when causal), and
+        # also over the pairs the mask allows (4*d per pair) where key lengths apply.
+        fl_tiled = w.counted_flops() / (t_tiled / n)
         rec = {"workload": name, "tiled_ms": round(t_tiled / n * 1e3, 4), "standard_ms": round(t_std / n * 1e3, 4),
+               "tiled_TFLOPs": round(fl_tiled / 1e12, 1),
+               "tiled_frac_of_peak": round(fl_tiled / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
                "speedup": round(t_std / t_tiled, 2), "workspace_bytes": need,
                "standard_algorithmic_bytes": nbytes,
                "standard_hbm_GBps": round(nbytes / avg / 1e9, 1)}
+        if lens_np is not None:
+            rec["tiled_TFLOPs_allowed_pairs"] = round(4 * w.d * allowed_scores(w, lens_np) / (t_tiled / n) / 1e12, 1)
         if name == main_name:
             rec["roofline"] = {"kernel": "std_scores_kernel + std_softmax_kernel + std_pv_kernel (whole call)",
                                "bound": "hbm", "achieved": round(nbytes / avg / 1e9, 1), "peak": PEAK_HBM_GBS,

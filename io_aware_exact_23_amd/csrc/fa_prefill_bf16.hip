@@ -53,8 +53,13 @@ __device__ __forceinline__ int k_perm(int r) {
   return (r & ~0xC) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2);
 }
 
-template <int D, int NQB>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+// WPE waves per SIMD, i.e. WPE workgroups per CU. At d = 64 a wave needs about 150 VGPRs and a
+// workgroup 32 KB of LDS, so three fit: with one wave per workgroup on each SIMD, the matrix work
+// of one wave can then run under the softmax of the others, which the kernel itself does not
+// arrange (13-16% faster than two on the GPT-2- and BERT-shaped workloads). d = 128 needs about
+// 250 VGPRs and keeps two.
+template <int D, int NQB, int WPE>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WPE, WPE)))
 void prefill_bf16_kernel(PrefillParams p) {
   using C = PrefillBf16Cfg<D, NQB>;
   __shared__ __attribute__((aligned(1024))) char stage_a[C::kStageBytes];
@@ -293,13 +298,13 @@ void prefill_bf16_kernel(PrefillParams p) {
   }
 }
 
-template <int D, int NQB>
+template <int D, int NQB, int WPE>
 static hipError_t launch_bf16(PrefillParams p, hipStream_t stream) {
   using C = PrefillBf16Cfg<D, NQB>;
   p.n_qtiles = (p.Nq + C::kBM - 1) / C::kBM;
   p.n_tiles = p.B * p.H * p.n_qtiles;
   if (p.n_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NQB>), dim3(p.n_tiles), dim3(C::kThreads), 0, stream, p);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NQB, WPE>), dim3(p.n_tiles), dim3(C::kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -307,8 +312,8 @@ static hipError_t launch_bf16(PrefillParams p, hipStream_t stream) {
 int prefill_bf16_rows_per_wg(int d) { return d == 64 ? PrefillBf16Cfg<64, 1>::kBM : PrefillBf16Cfg<128, 1>::kBM; }
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream) {
-  if (d == 64) return launch_bf16<64, 1>(p, stream);
-  return launch_bf16<128, 1>(p, stream);
+  if (d == 64) return launch_bf16<64, 1, 3>(p, stream);
+  return launch_bf16<128, 1, 2>(p, stream);
 }
 
 }  // namespace fa
