@@ -166,13 +166,37 @@ void decode_combine_kernel(DecodeParams p) {
   const float* lse_s = p.ws_lse + (size_t)bh * p.n_splits;
   const float* o_s = p.ws_o + (size_t)bh * p.n_splits * D;
 
+  // lse* = max over the partials: lanes take partials lane, lane + 64, ..., then a wave maximum.
   float M = -kInf;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, lse_s[s]);
+  for (int s = lane; s < n; s += 64) M = fmaxf(M, lse_s[s]);
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+  // Weighted sum over the partials in order, lanes over d. Partials go in groups of 8 whose loads
+  // are all issued before their arithmetic, so the loop waits for memory once per group rather
+  // than once per partial.
+  constexpr int kG = 8;
   float W = 0.0f;
   float acc[D / 64];
 #pragma unroll
   for (int t = 0; t < D / 64; ++t) acc[t] = 0.0f;
-  for (int s = 0; s < n; ++s) {
+  int s = 0;
+  for (; s + kG <= n; s += kG) {
+    float lg[kG], og[kG][D / 64];
+#pragma unroll
+    for (int u = 0; u < kG; ++u) {
+      lg[u] = lse_s[s + u];
+#pragma unroll
+      for (int t = 0; t < D / 64; ++t) og[u][t] = o_s[(size_t)(s + u) * D + lane + 64 * t];
+    }
+#pragma unroll
+    for (int u = 0; u < kG; ++u) {
+      const float wgt = fast_exp2(lg[u] - M);
+      W += wgt;
+#pragma unroll
+      for (int t = 0; t < D / 64; ++t) acc[t] = fmaf(wgt, og[u][t], acc[t]);
+    }
+  }
+  for (; s < n; ++s) {
     const float wgt = fast_exp2(lse_s[s] - M);
     W += wgt;
 #pragma unroll

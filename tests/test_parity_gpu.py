@@ -58,6 +58,8 @@ SMALL = [
     (1, 1, 64, 64, False, None),
     (3, 2, 300, 300, True, None),
     (2, 2, 2, 65, False, [65, 3]),
+    # padded batch without a causal mask: equal lengths, an empty sequence, a ragged tail
+    (5, 2, 150, 300, False, [130, 300, 17, 130, 0]),
 ]
 
 
@@ -91,7 +93,10 @@ def test_long_sequence_kernel(B, H, Nq, Nk, d, causal, lens):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B,H,Nk,lens", [(1, 1, 1, None), (2, 3, 700, [700, 1]), (3, 2, 513, [0, 256, 257]),
-                                          (4, 2, 8192, [8192, 1024, 4097, 5])])
+                                          (4, 2, 8192, [8192, 1024, 4097, 5]),
+                                          # more partials per sequence than a wave has lanes, and a
+                                          # count that is not a multiple of the combine's groups
+                                          (2, 2, 21000, [21000, 8321])])
 def test_decode_shapes(d, B, H, Nk, lens):
     q, k, v, lt, scale = _case(B, H, 1, Nk, d, "bf16", False, lens, seed=Nk + d)
     _check(q, k, v, lt, scale, False, "bf16", f"decode d={d} B={B} H={H} Nk={Nk} lens={lens}")
