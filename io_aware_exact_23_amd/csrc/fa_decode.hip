@@ -5,8 +5,8 @@
 // FlashDecoding as its IO-aware form (section "結論"). With one query there is no reuse of K/V,
 // so the pass is bound by HBM bandwidth: every valid key is read exactly once.
 //
-// Kernel 1 (split): one workgroup per (chunk of kDecodeChunk keys, h, b). Each wave streams 64
-// keys with 16-byte non-temporal loads (the keys are read once: keeping them in the caches only
+// Kernel 1 (split): one workgroup per (chunk of kDecodeChunk keys, h, b). Each wave streams
+// kDecodeKeysPerWave keys with 16-byte non-temporal loads (the keys are read once: keeping them in the caches only
 // evicts what other workgroups still need; +5.5% on the decode workload), kLanesPerKey lanes
 // per key row (whole rows per load instruction: perfectly coalesced), forms the dot products on
 // the vector ALUs, and keeps a local max, sum and unnormalised output. The waves merge through
@@ -20,10 +20,13 @@
 
 namespace fa {
 
-// Keys per chunk: two waves of 64 keys. Measured on the decode workload (64 x 32 heads, up to 8192
-// keys): 5.8 TB/s, against 5.7 with 256-key chunks, 4.4 with 512 and 5.4 with 64 (where the
-// partial outputs and their combine start to cost more than the finer balance gains).
+// Keys per chunk and per wave. Measured on the decode workload (64 x 32 heads, up to 8192 keys),
+// whole call: 128-key chunks of 4 waves x 32 keys 5.94 TB/s; of 2 waves x 64 keys 5.89 (with 8 x 16
+// the same); 256-key chunks 5.7, 512-key chunks 4.4; 96-key chunks 5.77, 64-key chunks 5.4-5.5,
+// where the partial outputs and their combine cost more than the finer balance gains.
 constexpr int kDecodeChunk = 128;
+constexpr int kDecodeKeysPerWave = 32;
+constexpr int kDecodeThreads = 64 * kDecodeChunk / kDecodeKeysPerWave;
 
 // Sum over aligned groups of N lanes (N a power of two <= 64).
 template <int N>
@@ -34,14 +37,15 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 template <int D, int CHUNK>
-__global__ __attribute__((amdgpu_flat_work_group_size(CHUNK, CHUNK)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * CHUNK / kDecodeKeysPerWave, 64 * CHUNK / kDecodeKeysPerWave)))
 void decode_split_kernel(DecodeParams p) {
-  constexpr int kWaves = CHUNK / 64;
+  constexpr int kWaves = CHUNK / kDecodeKeysPerWave;
   constexpr int kLanesPerKey = D / 8;          // 16 bytes (8 bf16) per lane
   constexpr int kKeysPerLoad = 64 / kLanesPerKey;
-  constexpr int kKeysPerWave = 64;
+  constexpr int kKeysPerWave = kDecodeKeysPerWave;
   constexpr int kRounds = kKeysPerWave / kKeysPerLoad;
   static_assert(kRounds * kKeysPerLoad == kKeysPerWave, "chunk must split evenly");
+  static_assert(kWaves * 64 >= D, "the merge gives one thread per output element");
 
   __shared__ float sm_m[kWaves], sm_l[kWaves];
   __shared__ float sm_o[kWaves][D];
@@ -217,10 +221,10 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream) 
   const dim3 grid1(p.n_splits, p.H, p.B);
   const dim3 grid2(p.B * p.H);
   if (d == 64) {
-    if (p.n_splits > 0) hipLaunchKernelGGL((decode_split_kernel<64, kDecodeChunk>), grid1, dim3(kDecodeChunk), 0, stream, p);
+    if (p.n_splits > 0) hipLaunchKernelGGL((decode_split_kernel<64, kDecodeChunk>), grid1, dim3(kDecodeThreads), 0, stream, p);
     hipLaunchKernelGGL((decode_combine_kernel<64, kDecodeChunk>), grid2, dim3(64), 0, stream, p);
   } else {
-    if (p.n_splits > 0) hipLaunchKernelGGL((decode_split_kernel<128, kDecodeChunk>), grid1, dim3(kDecodeChunk), 0, stream, p);
+    if (p.n_splits > 0) hipLaunchKernelGGL((decode_split_kernel<128, kDecodeChunk>), grid1, dim3(kDecodeThreads), 0, stream, p);
     hipLaunchKernelGGL((decode_combine_kernel<128, kDecodeChunk>), grid2, dim3(64), 0, stream, p);
   }
   return hipGetLastError();
