@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -66,6 +67,25 @@ int check_common(const void* q, const void* k, const void* v, const void* o, con
   return FA_OK;
 }
 
+// Compute units per XCD of the current device (the MI355X has 8 XCDs), 0 when the count is not a
+// multiple of 8 or cannot be read. Cached per device; the query has no side effects, so threads
+// that race to fill an entry store the same value.
+int cus_per_xcd() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDev) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c != 0) return c > 0 ? c : 0;
+  }
+  int n = 0;
+  const bool ok = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
+  const int per = (ok && n > 0 && n % 8 == 0) ? n / 8 : -1;
+  if (dev < kMaxDev) cache[dev].store(per, std::memory_order_relaxed);
+  return per > 0 ? per : 0;
+}
+
 fa::PrefillParams prefill_params(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int B, int H, int Nq, int Nk, float scale, int causal,
                                  const int32_t* kv_seqlens) {
@@ -86,6 +106,7 @@ fa::PrefillParams prefill_params(const void* q, const void* k, const void* v, vo
   // to exactly 1 and c*s is far below the resolution of the logsumexp: the results are those of c = 0.
   if (p.c == 0.0f) p.c = 1e-30f;
   p.causal = causal;
+  p.cus_per_xcd = cus_per_xcd();
   return p;
 }
 

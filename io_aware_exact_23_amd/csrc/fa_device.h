@@ -99,4 +99,27 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
   return xcd * per + (xcd < rem ? xcd : rem) + slot;
 }
 
+// Causal launches whose workgroups stay resident together. Within an XCD the hardware places the
+// workgroups it is handed breadth-first: local slots s, s + P, s + 2P, ... (P = CUs per XCD) share
+// a CU. Ordering each XCD's tiles heaviest first within a head (the plain causal order) then gives
+// one CU the same query-tile position of several heads, e.g. three of the heaviest tiles next to
+// a CU with three of the lightest. Instead, rank the XCD's tiles by weight (query tile descending,
+// heads cycling) and hand them out in serpentine order: ranks 0..P-1 to the CUs in order, the
+// next P in reverse, and so on, so that each CU's resident tiles sum to about the same work. The
+// XCD keeps the same contiguous range of tiles as xcd_remap gives it (same heads, same L2).
+// Applies when every XCD's range holds whole heads; otherwise returns false.
+__device__ __forceinline__ bool causal_serpentine(int wg, int n, int nq, int P, int& bh, int& qt) {
+  constexpr int kXcd = 8;
+  if (P <= 0 || n % (kXcd * nq) != 0) return false;
+  const int cnt = n / kXcd;        // tiles per XCD: whole heads
+  const int k = cnt / nq;          // heads per XCD
+  const int xcd = wg % kXcd;
+  const int s = wg / kXcd;         // local slot, in the order this XCD receives its workgroups
+  const int r = s / P, c = s - r * P;
+  const int j = ((r & 1) == 0 || (r + 1) * P > cnt) ? s : r * P + (P - 1 - c);  // weight rank
+  qt = nq - 1 - j / k;
+  bh = xcd * k + j % k;
+  return true;
+}
+
 }  // namespace fa

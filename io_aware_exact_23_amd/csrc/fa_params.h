@@ -18,6 +18,7 @@ struct PrefillParams {
   int causal;
   int n_qtiles;   // ceil(Nq / BM)
   int n_tiles;    // B * H * n_qtiles (the grid size)
+  int cus_per_xcd;  // compute units per XCD of the device (0 if unknown)
   // Generalised masks and layouts (the window / packed-sequence entry points only).
   int win_left, win_right;    // key j allowed for query i iff i-left <= j <= i+right; -1: no limit
   const int32_t* cu_q;        // packed sequences: [B+1] row offsets of each sequence, or nullptr

@@ -71,11 +71,16 @@ void prefill_bf16_kernel(PrefillParams p) {
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
-  // Work decomposition: workgroup -> (b, h, query tile); causal tiles heaviest first.
-  const int tile = xcd_remap(blockIdx.x, p.n_tiles);
-  const int bh = tile / p.n_qtiles;
-  int qt = tile - bh * p.n_qtiles;
-  if (p.causal) qt = p.n_qtiles - 1 - qt;
+  // Work decomposition: workgroup -> (b, h, query tile). Causal: tiles of similar total weight
+  // share a CU (serpentine order), or else heaviest first within a head. Otherwise tiles that
+  // share K/V share an XCD.
+  int bh, qt;
+  if (!(p.causal && causal_serpentine(blockIdx.x, p.n_tiles, p.n_qtiles, p.cus_per_xcd, bh, qt))) {
+    const int tile = xcd_remap(blockIdx.x, p.n_tiles);
+    bh = tile / p.n_qtiles;
+    qt = tile - bh * p.n_qtiles;
+    if (p.causal) qt = p.n_qtiles - 1 - qt;
+  }
   const int b = bh / p.H;
   const int q0 = qt * C::kBM;
   const int L = seq_len(p.kv_seqlens, b, p.Nk);
