@@ -8,7 +8,7 @@
 //   P_ij = exp(scale q_i.k_j - lse_i),  dV_j += P_ij dO_i,  dP_ij = dO_i . v_j,
 //   dS_ij = P_ij (dP_ij - D_i),  dQ_i += scale dS_ij k_j,  dK_j += scale dS_ij q_i.
 // Three kernels:
-//   bwd_delta_kernel  D_i = dO_i . O_i for every query row (fp32);
+//   bwd_delta_kernel  D_i = dO_i . O_i for every query row (fp32), several rows per wave;
 //   bwd_dq_kernel     one workgroup of 8 waves per 128 query rows, K/V tiles through LDS; per
 //                     SIMD one wave computes S^T = K Q^T and P^T, its partner dP^T = V dO^T,
 //                     then both dS^T and half each of dQ^T += K^T dS^T;
@@ -58,25 +58,44 @@ __device__ __forceinline__ void bwd_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// ---- D_i = dO_i . O_i (fp32), one wave per row, 8 bf16 per lane and step.
+// ---- D_i = dO_i . O_i (fp32). D/8 lanes share a row, 16 bytes of O and of dO each, so one wave
+// load covers 64/(D/8) whole rows; each lane takes kRowSteps rows, all loads issued before the
+// arithmetic. Per row: an in-lane sum of 8 products, then a sum over the row's lanes.
+template <int D>
+struct BwdDeltaCfg {
+  static constexpr int kLanesPerRow = D / 8;
+  static constexpr int kRowsPerLoad = 64 / kLanesPerRow;
+  static constexpr int kRowSteps = 4;
+  static constexpr int kRowsPerWave = kRowsPerLoad * kRowSteps;
+  static constexpr int kRowsPerWg = 4 * kRowsPerWave;  // 4 waves
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardParams p) {
+  using C = BwdDeltaCfg<D>;
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int w = threadIdx.x >> 6;
+  const int part = lane % C::kLanesPerRow;
   const int64_t rows = (int64_t)p.B * p.H * p.Nq;
-  if (row >= rows) return;
-  const uint16_t* o = static_cast<const uint16_t*>(p.o) + row * D;
-  const uint16_t* d = static_cast<const uint16_t*>(p.dout) + row * D;
-  float acc = 0.0f;
-  for (int c = lane * 8; c < D; c += 512) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(o + c);
-    const u32x4 bb = *reinterpret_cast<const u32x4*>(d + c);
+  const int64_t row0 = (int64_t)blockIdx.x * C::kRowsPerWg + w * C::kRowsPerWave + lane / C::kLanesPerRow;
+  u32x4 a[C::kRowSteps], bb[C::kRowSteps];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc += bf16_lo(a[t]) * bf16_lo(bb[t]) + bf16_hi(a[t]) * bf16_hi(bb[t]);
+  for (int r = 0; r < C::kRowSteps; ++r) {
+    const int64_t row = row0 + r * C::kRowsPerLoad;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    a[r] = row < rows ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.o) + row * D + part * 8) : z;
+    bb[r] = row < rows ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.dout) + row * D + part * 8) : z;
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) p.delta[row] = acc;
+  for (int r = 0; r < C::kRowSteps; ++r) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc += bf16_lo(a[r][t]) * bf16_lo(bb[r][t]) + bf16_hi(a[r][t]) * bf16_hi(bb[r][t]);
+#pragma unroll
+    for (int m = 1; m < C::kLanesPerRow; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    const int64_t row = row0 + r * C::kRowsPerLoad;
+    if (part == 0 && row < rows) p.delta[row] = acc;
+  }
 }
 
 template <int D>
@@ -740,7 +759,8 @@ hipError_t launch_backward(const BackwardParams& p, int d, hipStream_t stream) {
   if (bh == 0) return hipSuccess;
   const int64_t rows = bh * p.Nq;
   if (rows > 0) {
-    const dim3 g0((unsigned)((rows + 3) / 4));
+    const int per_wg = d == 64 ? BwdDeltaCfg<64>::kRowsPerWg : BwdDeltaCfg<128>::kRowsPerWg;
+    const dim3 g0((unsigned)((rows + per_wg - 1) / per_wg));
     if (d == 64) hipLaunchKernelGGL(bwd_delta_kernel<64>, g0, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL(bwd_delta_kernel<128>, g0, dim3(256), 0, stream, p);
     const dim3 g1((unsigned)(bh * ((p.Nq + 127) / 128)));
