@@ -65,5 +65,6 @@ def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: 
     assert np.all(lg[~fin] == lr[~fin]), f"{what}: lse infinities differ"
     lse_err = float(np.abs(lg[fin] - lr[fin]).max()) if fin.any() else 0.0
     msg = f"{what}: O max {max_err:.3e} mean {mean_err:.3e}, lse max {lse_err:.3e}"
+    print("parity", msg, flush=True)
     assert max_err <= max_tol and mean_err <= mean_tol and lse_err <= lse_tol, msg
     return max_err, mean_err, lse_err

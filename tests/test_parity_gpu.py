@@ -60,6 +60,9 @@ SMALL = [
     (2, 2, 2, 65, False, [65, 3]),
     # padded batch without a causal mask: equal lengths, an empty sequence, a ragged tail
     (5, 2, 150, 300, False, [130, 300, 17, 130, 0]),
+    # causal, B*H*n_qtiles a multiple of 8*n_qtiles (the serpentine work order), ragged last tile
+    (2, 4, 300, 300, True, None),
+    (4, 4, 1000, 1000, True, [1000, 999, 512, 3]),
 ]
 
 
