@@ -264,16 +264,16 @@ void prefill_bf16_kernel(PrefillParams p) {
     __syncthreads();
   };
 
-  // The Q loads must complete here, before the first tile's loads: the vector-memory counter is
-  // in order, so a Q load still pending inside the loop would make every wait for it also wait
-  // for the next tile's loads. The scheduling barriers keep the compiler from sinking them.
+  // The Q loads must complete before the loop: the vector-memory counter is in order, so a Q load
+  // still pending inside the loop would make every wait for it also wait for the next tile's
+  // loads. The first tile's loads go out right behind them and one wait covers both, so a
+  // workgroup pays one memory latency before its first tile, not two. The scheduling barriers
+  // keep the compiler from moving the loads across the wait.
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+  if (ntiles > 0) issue(0, stage_a);
   __builtin_amdgcn_sched_barrier(0);
-  if (ntiles > 0) {
-    issue(0, stage_a);
-    __builtin_amdgcn_s_waitcnt(0x3f70);
-  }
+  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): Q and tile 0
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
   for (int j = 0; j < ntiles; j += 2) {
     iteration(j, stage_a, stage_b);
