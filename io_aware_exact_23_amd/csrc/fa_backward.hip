@@ -146,11 +146,14 @@ __device__ __forceinline__ uint32_t bwd_off_tr(int w, int it, int lane) {
 //   phase A   S wave (w < 4):   S^T = K Q^T, P^T = 2^(c s - lse2) (masked) -> LDS as bf16;
 //             dP wave (w >= 4): dP^T = V dO^T, (dP^T - D) -> LDS as bf16;
 //   barrier
-//   phase B   both: dS^T = P^T (dP^T - D) from their own value and the partner's, then
-//             dQ^T += K^T dS^T for half of the head dimension each (S wave the low half);
+//   phase B   each wave one 32-key block (S wave keys 0..31, dP wave 32..63): dS^T = P^T (dP^T - D)
+//             of that block from its own value and the partner's, then dQ^T += K^T dS^T over
+//             the whole head dimension into its own accumulator;
 //   barrier (after this wave's copies of the next tile have landed).
 // 24 MFMAs per wave and tile, none recomputed, and the S wave's exponentials overlap the dP wave's
-// matrix work on the same SIMD.
+// matrix work on the same SIMD. Splitting phase B by keys rather than by head dimension means
+// each wave forms and exchanges only the half of dS it uses; the two partial dQ sums are added
+// once, at the end.
 template <int D>
 struct BwdQCfg {
   static constexpr int kWaves = 8;
@@ -166,6 +169,7 @@ struct BwdQCfg {
   static constexpr int kHalf = D / 64;                         // 32-d blocks of dQ per wave
   static_assert(kKiBPerWave * kWaves * 1024 == kTileBytes, "tile must split over the waves");
   static_assert(kXBase <= 65536, "stages must sit within the LDS immediate-offset range");
+  static_assert(8 * kHalf * 4096 <= kXBase, "the closing exchange of dQ halves fits in the stage area");
 };
 
 template <int D>
@@ -256,35 +260,34 @@ void bwd_dq_kernel(BackwardParams p) {
   const int ta = li >> 2, tb = li & 3;
   const int gp = (lane >> 4) & 1;
   const int rrow = swave ? r32 : bwd_perm(r32);
-  uint32_t rofs[D / 16], kt[2][C::kHalf];
+  uint32_t rofs[D / 16], kt[2][D / 32];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     rofs[ks] = (uint32_t)((swave ? 0 : C::kTileBytes) + rrow * C::kRowBytes + (((2 * ks + g) ^ bwd_swz<D>(rrow)) << 4));
     asm volatile("" : "+v"(rofs[ks]));
   }
-  const int db0 = swave ? 0 : C::kHalf;
 #pragma unroll
   for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
-    for (int j = 0; j < C::kHalf; ++j) {
+    for (int db = 0; db < D / 32; ++db) {
       const int r = 8 * rd + 4 * g + ta;
-      const int piece = (db0 + j) * 4 + 2 * gp + (tb >> 1);
-      kt[rd][j] = (uint32_t)(r * C::kRowBytes + ((piece ^ bwd_swz<D>(r)) << 4) + 8 * (tb & 1));
-      asm volatile("" : "+v"(kt[rd][j]));
+      const int piece = db * 4 + 2 * gp + (tb >> 1);
+      kt[rd][db] = (uint32_t)(r * C::kRowBytes + ((piece ^ bwd_swz<D>(r)) << 4) + 8 * (tb & 1));
+      asm volatile("" : "+v"(kt[rd][db]));
     }
   uint32_t xown = (uint32_t)(C::kXBase + qb * 8192 + (swave ? 0 : 4096) + lane * 16);
   uint32_t xoth = (uint32_t)(C::kXBase + qb * 8192 + (swave ? 4096 : 0) + lane * 16);
   asm volatile("" : "+v"(xown), "+v"(xoth));
 
-  f32x16 acc[C::kHalf];  // dQ^T: entry e of block j is dQ[qi][(db0 + j)*32 + 8(e/4) + 4g + e%4]
+  f32x16 acc[D / 32];  // this wave's keys' share of dQ^T: entry e of block db is dQ[qi][db*32 + 8(e/4) + 4g + e%4]
 #pragma unroll
-  for (int j = 0; j < C::kHalf; ++j)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+    for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
   f32x16 xs[2];  // P^T (S wave) or dP^T - D (dP wave) of the tile's two 32-key blocks
 
   constexpr int kNR = 2 * (D / 16);    // phase A: key block kb = m & 1, step ks = m >> 1
-  constexpr int kNT = 4 * C::kHalf;    // phase B: 16-key step u = m / kHalf, block j = m % kHalf
+  constexpr int kNT = 2 * (D / 32);   // phase B: 16-key step u2 = m / (D/32) of the wave's block, d block m % (D/32)
   constexpr int kAhead = 3;
 
   auto phase_a = [&](auto stage_tag, int k0) __attribute__((always_inline)) {
@@ -339,7 +342,8 @@ void bwd_dq_kernel(BackwardParams p) {
             }
             xo[t2] = pack_bf16(v2[0], v2[1]);
           }
-          *reinterpret_cast<u32x4*>(smem + ((kb * 2 + hh) * 1024 + (int)xown)) = xo;
+          // Only the partner's key block crosses over (the S wave's block is 0, the dP wave's 1).
+          if (kb == (kS ? 1 : 0)) *reinterpret_cast<u32x4*>(smem + ((kb * 2 + hh) * 1024 + (int)xown)) = xo;
         }
     };
     if (swave) {
@@ -352,36 +356,42 @@ void bwd_dq_kernel(BackwardParams p) {
 
   auto phase_b = [&](auto stage_tag) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_tag)::value;
-    auto fetch = [&](int m) -> bf16x8 __attribute__((always_inline)) {
-      const int u = m / C::kHalf, j = m % C::kHalf;
-      const int o = S * C::kStageBytes + u * 16 * C::kRowBytes;
-      const s16x4 a8[2] = {lds_read_tr16(smem + (o + (int)kt[0][j])), lds_read_tr16(smem + (o + (int)kt[1][j]))};
-      return __builtin_bit_cast(bf16x8, a8);
-    };
-    bf16x8 op[kNT];
+    // One code path per role: the wave's key block kbo must be known at compile time so that xs
+    // is indexed statically.
+    auto run = [&](auto role_tag) __attribute__((always_inline)) {
+      constexpr int kbo = decltype(role_tag)::value ? 0 : 1;
+      auto fetch = [&](int m) -> bf16x8 __attribute__((always_inline)) {
+        const int u = 2 * kbo + m / (D / 32), db = m % (D / 32);
+        const int o = S * C::kStageBytes + u * 16 * C::kRowBytes;
+        const s16x4 a8[2] = {lds_read_tr16(smem + (o + (int)kt[0][db])), lds_read_tr16(smem + (o + (int)kt[1][db]))};
+        return __builtin_bit_cast(bf16x8, a8);
+      };
+      bf16x8 op[kNT];
 #pragma unroll
-    for (int m = 0; m < kAhead; ++m) op[m] = fetch(m);
-    // dS^T = own value times the partner's (P^T times dP^T - D), as bf16 B operands.
-    bf16x8 dsk[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int m = 0; m < kAhead; ++m) op[m] = fetch(m);
+      // dS^T of this wave's key block = own value times the partner's (P^T times dP^T - D), as
+      // bf16 B operands.
+      bf16x8 dsk[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const u32x4 oth = *reinterpret_cast<const u32x4*>(smem + ((kb * 2 + hh) * 1024 + (int)xoth));
+        const u32x4 oth = *reinterpret_cast<const u32x4*>(smem + ((kbo * 2 + hh) * 1024 + (int)xoth));
         u32x4 xo;
 #pragma unroll
         for (int t2 = 0; t2 < 4; ++t2)
-          xo[t2] = pack_bf16(xs[kb][hh * 8 + 2 * t2] * bf16_lo(oth[t2]), xs[kb][hh * 8 + 2 * t2 + 1] * bf16_hi(oth[t2]));
-        dsk[kb][hh] = __builtin_bit_cast(bf16x8, xo);
+          xo[t2] = pack_bf16(xs[kbo][hh * 8 + 2 * t2] * bf16_lo(oth[t2]), xs[kbo][hh * 8 + 2 * t2 + 1] * bf16_hi(oth[t2]));
+        dsk[hh] = __builtin_bit_cast(bf16x8, xo);
       }
 #pragma unroll
-    for (int m = 0; m < kNT; ++m) {
+      for (int m = 0; m < kNT; ++m) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (m + kAhead < kNT) op[m + kAhead] = fetch(m + kAhead);
+        const int db = m % (D / 32);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], dsk[m / (D / 32)], acc[db], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      if (m + kAhead < kNT) op[m + kAhead] = fetch(m + kAhead);
-      const int u = m / C::kHalf, j = m % C::kHalf;
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], dsk[u >> 1][u & 1], acc[j], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    };
+    if (swave) run(std::true_type{});
+    else run(std::false_type{});
   };
 
   auto interval = [&](auto stage_tag, int t) __attribute__((always_inline)) {
@@ -409,17 +419,46 @@ void bwd_dq_kernel(BackwardParams p) {
   }
   bwd_wait_vmcnt<0>();
 
-  if (qi < p.Nq) {
-    uint16_t* dQg = static_cast<uint16_t*>(p.dq) + (size_t)bh * p.Nq * D + (size_t)qi * D;
+  // The two waves of a pair hold the sums over their own keys for the whole head dimension. Each
+  // writes the half the partner stores into the stage area (no longer read: the loop's last
+  // barrier has passed), then adds the partner's share of its own half and stores it. Block j of
+  // half h for pair qb sits at ((qb * 2 + h) * kHalf + j) * 4 KiB, 16 bytes per lane and quarter.
+  // One code path per role, so that every accumulator index is a compile-time constant (a
+  // run-time index would move the accumulators to scratch memory).
+  auto finish = [&](auto role_tag) __attribute__((always_inline)) {
+    constexpr bool kS = decltype(role_tag)::value;
+    constexpr int kOwn = kS ? 0 : C::kHalf, kOth = kS ? C::kHalf : 0;  // first d block of each half
+    constexpr int hOwn = kS ? 0 : 1, hOth = kS ? 1 : 0;
 #pragma unroll
     for (int j = 0; j < C::kHalf; ++j)
 #pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const u32x2 x = {pack_bf16(acc[j][4 * jq] * p.scale, acc[j][4 * jq + 1] * p.scale),
-                         pack_bf16(acc[j][4 * jq + 2] * p.scale, acc[j][4 * jq + 3] * p.scale)};
-        *reinterpret_cast<u32x2*>(dQg + (db0 + j) * 32 + 8 * jq + 4 * g) = x;
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const f32x4 x = {acc[kOth + j][4 * e4], acc[kOth + j][4 * e4 + 1], acc[kOth + j][4 * e4 + 2], acc[kOth + j][4 * e4 + 3]};
+        *reinterpret_cast<f32x4*>(smem + (((qb * 2 + hOth) * C::kHalf + j) * 4 + e4) * 1024 + lane * 16) = x;
       }
-  }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < C::kHalf; ++j)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(smem + (((qb * 2 + hOwn) * C::kHalf + j) * 4 + e4) * 1024 + lane * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[kOwn + j][4 * e4 + i] += x[i];
+      }
+    if (qi < p.Nq) {
+      uint16_t* dQg = static_cast<uint16_t*>(p.dq) + (size_t)bh * p.Nq * D + (size_t)qi * D;
+#pragma unroll
+      for (int j = 0; j < C::kHalf; ++j)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const u32x2 x = {pack_bf16(acc[kOwn + j][4 * jq] * p.scale, acc[kOwn + j][4 * jq + 1] * p.scale),
+                           pack_bf16(acc[kOwn + j][4 * jq + 2] * p.scale, acc[kOwn + j][4 * jq + 3] * p.scale)};
+          *reinterpret_cast<u32x2*>(dQg + (kOwn + j) * 32 + 8 * jq + 4 * g) = x;
+        }
+    }
+  };
+  if (swave) finish(std::true_type{});
+  else finish(std::false_type{});
 }
 
 // ---- dK, dV, two waves per SIMD. A workgroup of 8 waves owns 128 keys; waves w and w + 4 (one
