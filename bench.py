@@ -382,9 +382,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported. "
-              "The kernels shard over (batch, head) with no communication; see the design notes.",
-              file=sys.stderr)
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported. Attention over "
+              "(batch, head) shards with no communication: each GPU would run fa_fwd on its own "
+              "batches or heads.", file=sys.stderr)
         sys.exit(2)
 
     import torch
