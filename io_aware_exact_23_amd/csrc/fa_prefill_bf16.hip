@@ -99,17 +99,23 @@ void prefill_bf16_kernel(PrefillParams p) {
 
   const int qw0 = q0 + w * C::kQW;
   const int qw_last = min(qw0 + C::kQW, p.Nq) - 1;  // < qw0 when the wave has no rows
-  const float c = p.c;
-  const bool neg = c < 0.0f;
+  // Scores are handled in base-2 units t = c * (q.k). For c < 0 the kernel negates its copy of Q
+  // (a sign flip, exact in bf16 and in every product and sum) and uses -c, so below c > 0.
+  const bool neg = p.c < 0.0f;
+  const float c = neg ? -p.c : p.c;
 
   // Q tile -> registers, already in the B-operand layout of S^T = K Q^T.
   bf16x8 qreg[NQB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const uint32_t row = (uint32_t)(qw0 + qb * 32 + r32);
+    const uint32_t flip = neg ? 0x80008000u : 0u;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      qreg[qb][ks] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (row * D + ks * 16 + g * 8) * 2));
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 x = buf_load16(qrs, (row * D + ks * 16 + g * 8) * 2);
+      x ^= flip;
+      qreg[qb][ks] = __builtin_bit_cast(bf16x8, x);
+    }
   }
 
   f32x16 oacc[NQB][D / 32];
@@ -207,8 +213,28 @@ void prefill_bf16_kernel(PrefillParams p) {
         const int kb = x >> 4, i = x & 15;
         return kb * 32 + ((i >> 3) << 4) + (i & 7) < rem;
       };
+      // The raw scores of block qb again, from the K tile still in this stage (the softmax
+      // needs them only when it moves the offset after the row's first tile, which is rare).
+      auto recompute = [&](float (&x)[32]) __attribute__((always_inline)) {
+        f32x16 r[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) r[kb][i] = 0.0f;
+          const char* krow = Ks + kb * 32 * C::kRowBytes + krow_off;
+#pragma unroll
+          for (int ks = 0; ks < D / 16; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (((2 * ks + g) ^ kx) << 4));
+            r[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ks], r[kb], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[kb * 16 + i] = r[kb][i];
+      };
       bool rescaled;
-      const float alpha = softmax_tile<32, kMask>(s, valid, c, neg, m_used[qb], lsum[qb], rescaled);
+      const float alpha = softmax_tile_lazy<32, kMask>(s, valid, c, m_used[qb], lsum[qb], rescaled, recompute);
       if (rescaled) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)

@@ -109,4 +109,60 @@ __device__ __forceinline__ float softmax_tile(float (&s)[NV], ValidFn valid,
   return alpha;
 }
 
+// The same update with a lazier offset, for c > 0 (a caller with a negative scale negates its
+// copy of Q and passes |c|). On a row's first tile with an allowed key the offset goes to the row
+// maximum as above. After that the exponentials are taken against the offset as it stands, and
+// the offset moves to the row maximum only when a lane's sum of its NV values of p exceeds
+// kSumCap: with the offset held every p <= kSumCap, so nothing overflows, and most tiles need
+// neither the row maximum nor its cross-lane exchange (one FMA, one exponential and one addition
+// per score). In that rare case the raw scores, already overwritten, are produced again by
+// recompute(s). Arguments and result as in softmax_tile.
+constexpr float kSumCap = 4096.0f;
+template <int NV, bool kMask, typename ValidFn, typename RecomputeFn>
+__device__ __forceinline__ float softmax_tile_lazy(float (&s)[NV], ValidFn valid, float c,
+                                                   float& m_used, float& lsum, bool& rescaled,
+                                                   RecomputeFn recompute) {
+  // Exponent arguments c*s - off in place; masked keys get -inf, so their p is exactly 0.
+  auto args = [&](float off) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const float t = fmaf(s[i], c, -off);
+      if constexpr (kMask) s[i] = valid(i) ? t : -kInf;
+      else s[i] = t;
+    }
+  };
+  // Offset to the row maximum (and the factor for what was accumulated under the old offset),
+  // given the arguments in s taken against moff; then p.
+  auto to_row_max = [&](float moff) __attribute__((always_inline)) {
+    const float mt = pair32_max(tree_max(s)) + moff;  // row maximum of c*s; -inf if all masked
+    const float mn = fmaxf(m_used, mt);
+    const float alpha = (m_used == -kInf) ? 1.0f : fast_exp2(m_used - mn);
+    const float shift = ((mn == -kInf) ? 0.0f : mn) - moff;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) s[i] = fast_exp2(s[i] - shift);
+    lsum *= alpha;
+    m_used = mn;
+    return alpha;
+  };
+  float alpha = 1.0f;
+  if (wave_any(m_used == -kInf)) {
+    args(0.0f);
+    alpha = to_row_max(0.0f);
+    rescaled = true;
+  } else {
+    const float moff = m_used;
+    args(moff);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) s[i] = fast_exp2(s[i]);
+    rescaled = wave_any(tree_sum(s) > kSumCap);
+    if (rescaled) {
+      recompute(s);
+      args(moff);
+      alpha = to_row_max(moff);
+    }
+  }
+  lsum += tree_sum(s);
+  return alpha;
+}
+
 }  // namespace fa
