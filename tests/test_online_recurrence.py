@@ -63,3 +63,55 @@ def test_online_equals_definition(causal, lens, seed):
     fin = np.isfinite(lse_ref)
     assert np.array_equal(fin, np.isfinite(lse))
     assert np.max(np.abs(lse[fin] - lse_ref[fin])) <= 1e-12
+
+
+def lazy_offset_attention(q, k, v, scale, causal, lens, rng, cap):
+    """The recurrence with a lazy exponent offset, in base-2 units t = log2(e) * scale * q.k: p is
+    taken against an offset m that moves to the row maximum only on the row's first tile with an
+    allowed key or when the tile's sum of p exceeds `cap`; O and l carry the factor 2^-m, so any
+    offset gives the same result. This is the update the bf16 kernels run, written independently."""
+    c = scale / np.log(2.0)
+    bsz, heads, nq, d = q.shape
+    nk = k.shape[2]
+    o = np.zeros((bsz, heads, nq, v.shape[3]))
+    lse = np.zeros((bsz, heads, nq))
+    for b in range(bsz):
+        L = nk if lens is None else lens[b]
+        for h in range(heads):
+            for i in range(nq):
+                m, l, acc = -np.inf, 0.0, np.zeros(v.shape[3])
+                k0 = 0
+                while k0 < nk:
+                    cols = np.arange(k0, min(k0 + int(rng.integers(1, 9)), nk))
+                    ok = (cols < L) & (~causal | (cols <= i))
+                    t = np.where(ok, c * (k[b, h, cols] @ q[b, h, i]), -np.inf)
+                    off = 0.0 if m == -np.inf else m
+                    p = np.exp2(t - off)
+                    if (m == -np.inf and ok.any()) or p.sum() > cap:
+                        m_new = max(m, t.max())
+                        alpha = 1.0 if m == -np.inf else np.exp2(m - m_new)
+                        l, acc, m = alpha * l, alpha * acc, m_new
+                        p = np.exp2(t - m)
+                    l += p.sum()
+                    acc += p @ v[b, h, cols]
+                    k0 = cols[-1] + 1
+                o[b, h, i] = acc / l if l > 0 else 0.0
+                lse[b, h, i] = (m + np.log2(l)) * np.log(2.0) if l > 0 else -np.inf
+    return o, lse
+
+
+@pytest.mark.parametrize("cap", [1.5, 4.0, 4096.0])
+@pytest.mark.parametrize("causal,lens,seed", [(False, None, 11), (True, None, 12), (True, [30, 7, 0], 13)])
+def test_lazy_offset_equals_definition(cap, causal, lens, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((3, 1, 30, 5))
+    k = rng.standard_normal((3, 1, 30, 5))
+    # Scores that rise along the keys make the sum pass the cap and the offset move often.
+    k += np.linspace(0.0, 6.0, 30)[None, None, :, None] * np.sign(q.mean(axis=2, keepdims=True))
+    v = rng.standard_normal((3, 1, 30, 4))
+    o, lse = lazy_offset_attention(q, k, v, 0.7, causal, lens, rng, cap)
+    o_ref, lse_ref = attention_fwd(q, k, v, 0.7, causal, lens)
+    assert np.max(np.abs(o - o_ref)) <= 1e-12
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.max(np.abs(lse[fin] - lse_ref[fin])) <= 1e-12
