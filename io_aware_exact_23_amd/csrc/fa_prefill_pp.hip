@@ -212,14 +212,21 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
 
   // ---- HBM -> LDS. Wave w moves KiB blocks w*kKiBPerWave .. of each tile; in a block, lane i
   // fills LDS row rb + i/kNch, 16-byte slot i%kNch. A K row r holds key pp_k_perm(r) with piece
-  // (slot ^ (r % kNch)); a V row r holds key r with piece (slot ^ 4*(r % (kNch/4))).
+  // (slot ^ kswz(r)); a V row r holds key r with piece (slot ^ vswz(r)). At d = 128 a row fills
+  // the 256-byte bank line: kswz(r) = r % 16, vswz(r) = 4 * (r % 4). At d = 64 two rows share a
+  // line, and rows of one parity must differ in their pieces: kswz(r) = (r / 2) % 8 for the
+  // 16-byte K reads of 16 consecutive rows, vswz(r) = 4 * ((r ^ r / 2) % 2) for the transposed V
+  // reads of 4 consecutive rows (the d = 128 forms would put rows r and r + 8, and r and r + 2,
+  // on the same banks).
+  auto kswz = [](int r) { return (C::kRowBytes >= 256 ? r : r >> 1) % C::kNch; };
+  auto vswz = [](int r) { return C::kRowBytes >= 256 ? 4 * (r % (C::kNch / 4)) : 4 * ((r ^ (r >> 1)) & 1); };
   uint32_t koff[C::kKiBPerWave], voff[C::kKiBPerWave];
 #pragma unroll
   for (int it = 0; it < C::kKiBPerWave; ++it) {
     const int row = (w * C::kKiBPerWave + it) * C::kRowsPerKiB + lane / C::kNch;
     const int slot = lane % C::kNch;
-    koff[it] = (uint32_t)(pp_k_perm(row) * C::kRowBytes + ((slot ^ (row % C::kNch)) << 4));
-    voff[it] = (uint32_t)(row * C::kRowBytes + ((slot ^ (4 * (row % (C::kNch / 4)))) << 4));
+    koff[it] = (uint32_t)(pp_k_perm(row) * C::kRowBytes + ((slot ^ kswz(row)) << 4));
+    voff[it] = (uint32_t)(row * C::kRowBytes + ((slot ^ vswz(row)) << 4));
   }
   // Unit u = (K tile i_lo + u, V tile i_lo + u - 1), offsets relative to the views' start. V tile
   // i_lo - 1 and K tile n lie outside the buffer range and read as zeros (the unsigned offset of
@@ -238,7 +245,7 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
   // ---- LDS -> operands (loop-invariant per-lane byte offsets).
   // K A-operand: lane (r32, g) reads row kb*32 + r32, piece 2*ks + g.
   const int krow_off = r32 * C::kRowBytes;
-  const int kx = r32 % C::kNch;
+  const int kx = kswz(r32);
   // V^T A-operand via transposed reads: in 16-lane group grp16 = lane/16 (gp = grp16%2,
   // g = grp16/2), lane 4a+b addresses key (kb*32 + hh*16 + 8*g + 4*t + a), d = db*32 + 16*gp + 4*b.
   const int li = lane & 15;
@@ -248,7 +255,7 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     const int piece = db * 4 + 2 * gp + (tb >> 1);
-    const int sw = 4 * (ta % (C::kNch / 4));
+    const int sw = vswz(ta);  // rows 8g + ta (+4): bits 0 and 1 are ta's
     vt_off[db] = (8 * g + ta) * C::kRowBytes + ((piece ^ sw) << 4) + 8 * (tb & 1);
   }
   // Per-lane LDS byte offsets of every operand read, computed once. The immediate offset field of
