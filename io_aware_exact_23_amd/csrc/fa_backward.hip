@@ -107,18 +107,22 @@ struct BwdCfg {
   static constexpr int kKiBPerWave = kTileBytes / 1024 / 4;
 };
 
-// 16-byte piece swizzle of LDS row r, for tiles the backward kernels read both ways: as rows
-// (ds_read_b128, 16 consecutive rows, one piece: the swizzle is a bijection on each aligned block
-// of 16 rows, and on each half of such a block taken in bwd_perm order it is distinct modulo 8)
-// and transposed (ds_read_b64_tr_b16, a 16-lane group reading two adjacent pieces of 4
-// consecutive rows: swizzle / 2 is distinct over each aligned group of 4 rows, and modulo 4 over
-// each aligned pair). So neither read shares a bank within a pass, whether the LDS serves 128 or
-// 256 bytes a cycle. With x = r % 16 (bits x3 x2 x1 x0): d = 128 (16 pieces per row)
-// (x3, x1, x0, x2 ^ x3); d = 64 (8 pieces; two rows share 256 bytes) (x0 ^ x1 ^ x3, x0 ^ x2, x1).
+// 16-byte piece swizzle of LDS row r, for tiles the backward kernels read both as rows and
+// transposed. The LDS serves 256 bytes a pass: 16 lanes of a 16-byte row read (ds_read_b128), 32
+// lanes of an 8-byte transposed read (ds_read_b64_tr_b16). Row reads take one piece of 16 rows of
+// an aligned block of 16 (in bwd_perm order or not), so the swizzle must be a bijection on each
+// such block. Transposed reads take, in each pass, two 16-lane groups: 4 consecutive rows (r % 4
+// varying) times 4 pieces (two adjacent pieces per group, the groups' pieces 2 apart).
+// With x = r % 16 (bits x3 x2 x1 x0):
+// d = 128 (16 pieces per row, one row per 256-byte bank line): (x1, x0, x3, x2). Bits 3 and 2 of
+// the swizzle are a bijection of r % 4, which separates the 4 rows of a transposed pass while
+// the pieces (bits 1 and 0) separate the lanes within a row. An earlier form, (x3, x1, x0, x2^x3),
+// let rows r and r + 1 collide in those passes: one conflict cycle per three active ones.
+// d = 64 (8 pieces; two rows share a 256-byte line): (x0 ^ x1 ^ x3, x0 ^ x2, x1).
 template <int D>
 __device__ __forceinline__ int bwd_swz(int r) {
   const int x0 = r & 1, x1 = (r >> 1) & 1, x2 = (r >> 2) & 1, x3 = (r >> 3) & 1;
-  if (D == 128) return (x3 << 3) | (x1 << 2) | (x0 << 1) | (x2 ^ x3);
+  if (D == 128) return (x1 << 3) | (x0 << 2) | (x3 << 1) | x2;
   return ((x0 ^ x1 ^ x3) << 2) | ((x0 ^ x2) << 1) | x1;
 }
 
