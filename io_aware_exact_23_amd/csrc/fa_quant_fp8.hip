@@ -12,7 +12,7 @@
 //                          largest bf16 magnitude bit pattern (exact, no float compare);
 //   quant_rows_kernel      [N][D] output, 16 elements per thread and step;
 //   quant_transpose_kernel [D][cols] output (V^T, cols = N rounded up to 64), one 64-key tile
-//                          per workgroup, transposed through LDS.
+//                          per workgroup, transposed in registers.
 #include "fa_device.h"
 #include "fa_params.h"
 
@@ -88,7 +88,15 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantParams p) {
 // V^T: tile of keys k0 .. k0+63 of one slice; LDS tile t[d][64] bytes.
 template <int D>
 __global__ __launch_bounds__(256) void quant_transpose_kernel(QuantParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t t[D * 64];
+  // One 64-key tile per workgroup, transposed in registers: thread (c8, kq) takes keys
+  // 4kq .. 4kq+3 of 8-element piece c8 (kq = 0..15 within a wave, so a wave's loads cover 64-byte
+  // runs of 16 rows), quantises them, and gathers byte j of the four keys into one word per
+  // dimension, which goes to V^T[8 c8 + j][k0 + 4 kq]: each store instruction writes 64-byte runs.
+  // No LDS: an earlier version staged the tile through LDS with byte writes that put 16 lanes
+  // on one bank.
+  constexpr int kThreadsPerRowPiece = 16;          // kq
+  constexpr int kPieces = D / 8;                   // c8: 8 (d = 64) or 16 (d = 128)
+  constexpr int kPasses = kPieces * kThreadsPerRowPiece / 256;  // 1 for d = 128; d = 64 uses half
   const int bh = blockIdx.x;
   const float s = slice_scale(p, bh);
   if (blockIdx.y == 0 && threadIdx.x == 0) p.descale[bh] = s;
@@ -96,32 +104,31 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(QuantParams p) {
   if (k0 >= p.cols) return;
   const int L = seq_len(p.lens, bh / p.H, p.N);
   const uint16_t* src = p.x + (size_t)bh * p.N * D;
-  constexpr int kPieces = 64 * D / 8;  // 8 bf16 per piece
+  uint8_t* dst = p.y + (size_t)bh * D * p.cols + k0;
+  const int kq = threadIdx.x % kThreadsPerRowPiece;
+  const int c8 = threadIdx.x / kThreadsPerRowPiece;
+  if (kPasses == 0 && c8 >= kPieces) return;  // d = 64: 128 threads cover the tile
+  uint32_t lo[4], hi[4];
 #pragma unroll
-  for (int it = 0; it < kPieces / 256; ++it) {
-    const int pc = it * 256 + threadIdx.x;
-    const int r = pc / (D / 8), c8 = pc % (D / 8);
-    const int key = k0 + r;
-    uint32_t lo = 0u, hi = 0u;
+  for (int i = 0; i < 4; ++i) {
+    const int key = k0 + 4 * kq + i;
+    lo[i] = 0u;
+    hi[i] = 0u;
     if (key < L) {
       const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)key * D) + c8);
-      lo = quant4(w[0], w[1], s);
-      hi = quant4(w[2], w[3], s);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      t[(8 * c8 + j) * 64 + r] = (uint8_t)(lo >> (8 * j));
-      t[(8 * c8 + 4 + j) * 64 + r] = (uint8_t)(hi >> (8 * j));
+      lo[i] = quant4(w[0], w[1], s);  // dimensions 8 c8 + 0..3
+      hi[i] = quant4(w[2], w[3], s);  // dimensions 8 c8 + 4..7
     }
   }
-  __syncthreads();
-  uint8_t* dst = p.y + (size_t)bh * D * p.cols + k0;
+  auto gather = [](const uint32_t (&x)[4], int j) {
+    const int sh = 8 * j;
+    return ((x[0] >> sh) & 0xffu) | (((x[1] >> sh) & 0xffu) << 8) | (((x[2] >> sh) & 0xffu) << 16) |
+           (((x[3] >> sh) & 0xffu) << 24);
+  };
 #pragma unroll
-  for (int it = 0; it < D * 4 / 256; ++it) {
-    const int pc = it * 256 + threadIdx.x;
-    const int d = pc >> 2, part = pc & 3;
-    *reinterpret_cast<u32x4*>(dst + (size_t)d * p.cols + 16 * part) =
-        *reinterpret_cast<const u32x4*>(t + d * 64 + 16 * part);
+  for (int j = 0; j < 4; ++j) {
+    *reinterpret_cast<uint32_t*>(dst + (size_t)(8 * c8 + j) * p.cols + 4 * kq) = gather(lo, j);
+    *reinterpret_cast<uint32_t*>(dst + (size_t)(8 * c8 + 4 + j) * p.cols + 4 * kq) = gather(hi, j);
   }
 }
 
