@@ -61,13 +61,16 @@ __global__ __launch_bounds__(256) void std_scores_kernel(StandardParams p) {
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kg, (uint32_t)kvalid * kRowBytes);
 
   // K block -> LDS: lane i of 1 KiB block bl fills row bl*(1024/kRowBytes) + i/kNch, slot i%kNch,
-  // which holds piece slot ^ (row % kNch) of that key row.
+  // which holds piece slot ^ kswz(row) of that key row. kswz keeps the 16 rows of one 16-byte read
+  // pass on distinct banks: r % 16 when a row fills the 256-byte bank line (d = 128), (r / 2) % 8
+  // when two rows share it (d = 64; r % 8 there puts rows r and r + 8 on the same banks).
+  auto kswz = [](int r) { return (kRowBytes >= 256 ? r : r >> 1) % kNch; };
 #pragma unroll
   for (int it = 0; it < kLoads; ++it) {
     const int bl = w * kLoads + it;
     const int row = bl * (1024 / kRowBytes) + lane / kNch;
     const int slot = lane % kNch;
-    buf_load16_lds(krs, ks_lds + bl * 1024, (uint32_t)(row * kRowBytes + ((slot ^ (row % kNch)) << 4)));
+    buf_load16_lds(krs, ks_lds + bl * 1024, (uint32_t)(row * kRowBytes + ((slot ^ kswz(row)) << 4)));
   }
 
   // A operands (Q rows): lane (r32, g) holds Q[row 64w + 32 rb + r32][16 ks + 8 g .. +8].
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(256) void std_scores_kernel(StandardParams p) {
 
   float* Sg = p.s + (size_t)bh * p.Nq * p.ld;
   const int i0 = qt * kStdRows + w * 64;
-  const int kx = r32 % kNch;
+  const int kx = kswz(r32);
   for (int nb = 0; nb < kStdKeys / 32; ++nb) {
     // B operand (K^T): lane (r32, g) holds K[key 32 nb + r32][16 ks + 8 g .. +8].
     const char* krow = ks_lds + (nb * 32 + r32) * kRowBytes;
@@ -329,13 +332,16 @@ __global__ __launch_bounds__(256) void std_pv_kernel(StandardParams p) {
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vg, (uint32_t)L * C::kRowBytes);
 
   // V tile -> LDS: wave w moves KiB blocks w*kKiBPerWave ..; lane i fills row rb + i/kNch,
-  // 16-byte slot i%kNch, which holds piece slot ^ 4*(row % (kNch/4)) of key row `row`.
+  // 16-byte slot i%kNch, which holds piece slot ^ vswz(row) of key row `row`. vswz keeps the 4
+  // rows of one transposed read pass on distinct banks: 4 * (r % 4) when a row fills the 256-byte
+  // bank line (d = 128), 4 * ((r ^ r / 2) % 2) when two rows share it (d = 64).
+  auto vswz = [](int r) { return C::kRowBytes >= 256 ? 4 * (r % (C::kNch / 4)) : 4 * ((r ^ (r >> 1)) & 1); };
   uint32_t voff[C::kKiBPerWave];
 #pragma unroll
   for (int it = 0; it < C::kKiBPerWave; ++it) {
     const int row = (w * C::kKiBPerWave + it) * C::kRowsPerKiB + lane / C::kNch;
     const int slot = lane % C::kNch;
-    voff[it] = (uint32_t)(row * C::kRowBytes + ((slot ^ (4 * (row % (C::kNch / 4)))) << 4));
+    voff[it] = (uint32_t)(row * C::kRowBytes + ((slot ^ vswz(row)) << 4));
   }
   auto issue_v = [&](int tile, char* stage) {
     const uint32_t base = (uint32_t)tile * C::kTileBytes;
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(256) void std_pv_kernel(StandardParams p) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     const int piece = db * 4 + 2 * gp + (tb >> 1);
-    const int sw = 4 * (ta % (C::kNch / 4));
+    const int sw = vswz(ta);  // rows 16u + 8kg + ta (+4): bits 0 and 1 are ta's
     vt_off[db] = (8 * g + ta) * C::kRowBytes + ((piece ^ sw) << 4) + 8 * (tb & 1);
   }
 
