@@ -218,18 +218,19 @@ def test_huge_scores_long_sequence_kernel():
     _check(q, k, v, lt, 2.0, True, "bf16", "huge scores, long sequence")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
-def test_rising_scores_move_the_offset_often(causal):
+def test_rising_scores_move_the_offset_often(causal, d):
     # Scores that grow steadily with the key index (one coordinate of every query is 1 and the
     # same coordinate of key j is ~0.26*j), so the row maximum keeps rising: the exponent offset
     # of the kernels must move every few tiles, each time rescaling O and the row sum. Both
     # kernels (Nq = 130 and Nq = 2048) see the same kind of input.
     for Nq in (130, 2048):
-        q, k, v, _, _ = _case(1, 2, Nq, Nq, 64, "bf16", causal, None, seed=63, std=0.5)
+        q, k, v, _, _ = _case(1, 2, Nq, Nq, d, "bf16", causal, None, seed=63, std=0.5)
         q[..., 0] = 1.0
         ramp = 0.26 * torch.arange(Nq, device=DEV, dtype=torch.float32)
         k[..., 0] = ramp.to(q.dtype)
-        _check(q, k, v, None, 0.125, causal, "bf16", f"rising scores Nq={Nq} causal={causal}")
+        _check(q, k, v, None, 0.125, causal, "bf16", f"rising scores d={d} Nq={Nq} causal={causal}")
 
 
 @pytest.mark.parametrize("scale", [-0.3, 0.0])
