@@ -110,3 +110,42 @@ def test_backward_no_query_rows_zero_key_gradients():
     fa.fa_bwd(q, k, v, o, q, lse, q, dk, dv, 1, 2, 0, 70, 64, 0.125, 0, None)
     torch.cuda.synchronize()
     assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def _workload_grads(w):
+    """The gradients fa_bwd returns for a named workload, on the inputs and upstream gradient the
+    benchmark times it with."""
+    q, k, v, lt = inputs.make(w, DEV)
+    do = inputs.normal((w.B, w.H, w.Nq, w.d), w.seed + 7, DEV, "bf16", 1.0)
+    o, lse = fa.attention(q, k, v, scale=w.scale, causal=w.causal, kv_seqlens=lt)
+    dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do, scale=w.scale, causal=w.causal,
+                                       kv_seqlens=lt)
+    torch.cuda.synchronize()
+    lens = None if lt is None else [int(x) for x in lt.to("cpu").tolist()]
+    return q, k, v, do, lens, (dq, dk, dv)
+
+
+def _check_heads(w, heads):
+    q, k, v, do, lens, grads = _workload_grads(w)
+    for g in grads:
+        assert torch.isfinite(g).all(), f"{w.name}: non-finite gradient"
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = attention_bwd(to_f64(q[sl]), to_f64(k[sl]), to_f64(v[sl]), to_f64(do[sl]), f32(w.scale),
+                            causal=w.causal, kv_seqlens=None if lens is None else [lens[b]])
+        for name, g, r in zip(("dQ", "dK", "dV"), grads, ref):
+            _grad_close(to_f64(g[sl]), r, f"{name} {w.name} b={b} h={h}")
+
+
+def test_backward_gpt2_small_causal_workload():
+    """Every head of the GPT-2-small causal shape (B 8, H 12, N 1024, d 64)."""
+    w = configs.GPT2_SMALL_CAUSAL
+    _check_heads(w, [(b, h) for b in range(w.B) for h in range(w.H)])
+
+
+def test_backward_long_causal_16k_workload_two_heads():
+    """Two whole heads (first and last) of the 16K causal shape (B 2, H 16, N 16384, d 128), every
+    row and key of each, in the launch configuration the benchmark times; the remaining heads are
+    checked for finiteness only (the fp64 oracle takes about 12 s and 13 GB per head)."""
+    w = configs.LONG_CAUSAL_16K
+    _check_heads(w, [(0, 0), (w.B - 1, w.H - 1)])
