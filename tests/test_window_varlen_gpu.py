@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import io_aware_exact_23_amd as fa
-from io_aware_exact_23_amd import inputs
+from io_aware_exact_23_amd import configs, inputs
 from oracle import attention_fwd
 
 from parity_util import compare, f32, run_oracle, to_f64
@@ -151,3 +151,44 @@ def test_varlen_sequences_are_isolated():
     for a, b in ((0, 300), (2400, 2490)):
         assert torch.equal(o1[:, a:b].view(torch.int16), o2[:, a:b].view(torch.int16))
         assert torch.equal(l1[:, a:b], l2[:, a:b])
+
+
+def _sampled_rows(n, seed):
+    g = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(0, 8), np.arange(4088, 4104), g.integers(0, n, 32),
+                                     np.arange(n - 8, n)]))
+
+
+def test_sliding_window_16k_workload_sampled_rows():
+    """The 4096-key causal sliding window on the 16K causal shape (B 2, H 16, N 16384, d 128), as
+    timed by the benchmark; rows on both sides of the point where the window starts to slide."""
+    w = configs.LONG_CAUSAL_16K
+    q, k, v, _ = inputs.make(w, DEV)
+    window = (4095, 0)
+    o, lse = fa.attention(q, k, v, scale=w.scale, window=window)
+    torch.cuda.synchronize()
+    rows = _sampled_rows(w.Nq, 21)
+    o_ref, lse_ref = run_oracle(q, k, v, w.scale, False, None, rows=rows, window=window)
+    rt = torch.as_tensor(rows, device=DEV)
+    compare(to_f64(o[:, :, rt]), to_f64(lse[:, :, rt]), o_ref, lse_ref, "bf16",
+            what=f"{w.name} window {window} sampled rows")
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_packed_16k_workload_sampled_rows():
+    """The 16K causal shape's two sequences packed end to end, head-major ([H, 2*16384, d]), causal
+    within each sequence, as timed by the benchmark."""
+    w = configs.LONG_CAUSAL_16K
+    q, k, v, _ = inputs.make(w, DEV)
+    T = w.B * w.Nq
+    qp, kp, vp = (t.permute(1, 0, 2, 3).reshape(w.H, T, w.d).contiguous() for t in (q, k, v))
+    cu = torch.arange(0, T + 1, w.Nq, dtype=torch.int32, device=DEV)
+    o, lse = fa.varlen_attention(qp, kp, vp, cu, cu, w.Nq, scale=w.scale, window=(-1, 0))
+    torch.cuda.synchronize()
+    rows = _sampled_rows(w.Nq, 22)
+    o_ref, lse_ref = run_oracle(q, k, v, w.scale, True, None, rows=rows)
+    rt = torch.as_tensor(rows, device=DEV)
+    og = torch.stack([o[:, b * w.Nq + rt] for b in range(w.B)])
+    lg = torch.stack([lse[:, b * w.Nq + rt] for b in range(w.B)])
+    compare(to_f64(og), to_f64(lg), o_ref, lse_ref, "bf16", what=f"{w.name} packed sampled rows")
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
