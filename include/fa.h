@@ -17,6 +17,8 @@
  *   kv_seqlens : int32 [B] valid key count per sequence, clamped to [0, Nk] on the device;
  *                NULL means every sequence has Nk valid keys.
  * q, k, v and o must be 16-byte aligned; lse and kv_seqlens 4-byte aligned.
+ * One head's q, k or v (max(Nq, Nk) * d * element size) must stay below 2^31 bytes, else
+ * FA_ERR_UNSUPPORTED: the kernels address a head through 32-bit buffer offsets.
  *
  * Ownership. Every pointer is device memory owned by the caller. The library reads q, k, v and
  * kv_seqlens, writes only o and lse (and, for Nq == 1, a workspace it allocates and frees
@@ -42,7 +44,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARGUMENT = -1, /* null pointer, negative size, misalignment, non-finite scale */
-  FA_ERR_UNSUPPORTED = -2,      /* d not in {64, 128}; causal with Nq != Nk; sizes past int32  */
+  FA_ERR_UNSUPPORTED = -2,      /* d not in {64, 128}; causal with Nq != Nk; sizes too large     */
   FA_ERR_HIP = -3               /* the HIP runtime refused a launch or an allocation           */
 } fa_status_t;
 

@@ -44,10 +44,13 @@ int fail_hip(hipError_t e, const char* where) {
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
-// Checks shared by both entry points. Returns FA_OK, an error, or 1 for "valid no-op".
+// Checks shared by the entry points. Returns FA_OK, an error, or 1 for "valid no-op".
+// elem_bytes is the size of one element of q, k and v. The kernels address one head's rows
+// through buffer views with 32-bit sizes and byte offsets, so a head's Q, K or V must stay below
+// 2^31 bytes.
 int check_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                 const int32_t* kv_seqlens) {
+                 const int32_t* kv_seqlens, int elem_bytes) {
   g_last_error[0] = '\0';
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "B, H, Nq, Nk must be >= 0");
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d must be 64 or 128");
@@ -57,6 +60,8 @@ int check_common(const void* q, const void* k, const void* v, const void* o, con
   const int64_t bh = (int64_t)B * H;
   if (bh > std::numeric_limits<int32_t>::max())
     return fail(FA_ERR_UNSUPPORTED, "B*H exceeds int32");
+  if ((int64_t)std::max(Nq, Nk) * d * elem_bytes >= ((int64_t)1 << 31))
+    return fail(FA_ERR_UNSUPPORTED, "one head's q, k or v must stay below 2^31 bytes");
   if (bh == 0 || Nq == 0) return 1;
   if (!q || !o || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "q, o and lse must be non-null");
   if (Nk > 0 && (!k || !v)) return fail(FA_ERR_INVALID_ARGUMENT, "k and v must be non-null");
@@ -115,7 +120,7 @@ fa::PrefillParams prefill_params(const void* q, const void* k, const void* v, vo
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int H, int Nq, int Nk, int d, float scale, int causal,
                       const int32_t* kv_seqlens, void* stream) {
-  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens);
+  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, 2);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -169,7 +174,7 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
 extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           int B, int H, int Nq, int Nk, int d, float scale, int causal,
                           const int32_t* kv_seqlens, void* stream) {
-  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens);
+  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, 4);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
   const int64_t n_wg = (int64_t)B * H * ((Nq + 127) / 128);
@@ -183,7 +188,7 @@ extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float*
 extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
                       int d, float scale, int causal, const int32_t* kv_seqlens, void* stream) {
-  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens);
+  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, 2);
   if (st == 1) {
     // No query rows: dK and dV are still defined, zero, when there are keys (the dK/dV kernel
     // writes them without visiting any query tile; the other kernels have no rows to run on).
@@ -259,7 +264,7 @@ extern "C" int fa_fwd_window(const void* q, const void* k, const void* v, void* 
   const bool bounded = window_left >= 0 || window_right >= 0;
   int st = check_window(window_left, window_right);
   if (st != FA_OK) return st;
-  st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, 0, kv_seqlens);
+  st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, 0, kv_seqlens, 2);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
   if (bounded && Nq != Nk) return fail(FA_ERR_UNSUPPORTED, "a bounded window needs Nq == Nk");
@@ -329,7 +334,7 @@ extern "C" int fa_std_fwd(const void* q, const void* k, const void* v, void* o, 
                           int B, int H, int Nq, int Nk, int d, float scale, int causal,
                           const int32_t* kv_seqlens, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens);
+  int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, 2);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
   const int64_t ld = std_ld(Nk);
@@ -430,15 +435,15 @@ extern "C" int fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, const
                           const float* descale_k, const float* descale_v, void* o, float* lse,
                           int B, int H, int Nq, int Nk, int d, float scale, int causal,
                           const int32_t* kv_seqlens, void* stream) {
-  int st = check_common(q8, k8, vt8, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens);
+  int st = check_common(q8, k8, vt8, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, 1);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
   if ((descale_q && !aligned(descale_q, 4)) || (descale_k && !aligned(descale_k, 4)) ||
       (descale_v && !aligned(descale_v, 4)))
     return fail(FA_ERR_INVALID_ARGUMENT, "descale arrays must be 4-byte aligned");
-  // Per-(b, h) buffer views are addressed with 32-bit byte offsets.
-  if ((int64_t)fa_fp8_vt_cols(Nk) * d >= ((int64_t)1 << 31) || (int64_t)Nq * d >= ((int64_t)1 << 31))
-    return fail(FA_ERR_UNSUPPORTED, "one head's q8, k8 or vt8 must stay below 2^31 bytes");
+  // The transposed V is padded to whole 64-key tiles: its head must also stay below 2^31 bytes.
+  if ((int64_t)fa_fp8_vt_cols(Nk) * d >= ((int64_t)1 << 31))
+    return fail(FA_ERR_UNSUPPORTED, "one head's q, k or v must stay below 2^31 bytes");
   const int bm = fa::prefill_fp8_rows_per_wg();
   const int64_t n_wg = (int64_t)B * H * ((Nq + bm - 1) / bm);
   if (n_wg > std::numeric_limits<int32_t>::max()) return fail(FA_ERR_UNSUPPORTED, "grid too large");

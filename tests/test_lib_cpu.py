@@ -86,6 +86,8 @@ ENTRY = {"fa_fwd": lambda **kw: fa.fa_fwd(**kw), "fa_fwd_f32": lambda **kw: fa.f
     (dict(lse=A + 2), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
     (dict(kv_seqlens=A + 1), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
     (dict(B=70000, H=70000), fa.FA_ERR_UNSUPPORTED, "int32"),
+    (dict(Nk=1 << 23, d=128), fa.FA_ERR_UNSUPPORTED, "2^31 bytes"),
+    (dict(Nq=1 << 23, Nk=1 << 23, d=128, causal=1), fa.FA_ERR_UNSUPPORTED, "2^31 bytes"),
 ])
 def test_argument_errors(fn, args, status, needle):
     call = dict(q=A, k=A, v=A, o=A, lse=A, B=2, H=3, Nq=8, Nk=8, d=64, scale=0.125, causal=0,
@@ -220,6 +222,7 @@ BWD = dict(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, dk=A, dv=A, B=2, H=3, Nq=8, 
     (dict(dout=A + 8), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
     (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARGUMENT, "finite"),
     (dict(Nq=0, dk=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(Nq=1 << 24, d=64), fa.FA_ERR_UNSUPPORTED, "2^31 bytes"),
 ])
 def test_backward_argument_errors(args, status, needle):
     call = dict(BWD)
@@ -254,6 +257,7 @@ FP8 = dict(q8=A, k8=A, vt8=A, descale_q=A, descale_k=A, descale_v=A, o=A, lse=A,
     (dict(vt8=A + 8), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
     (dict(descale_k=A + 2), fa.FA_ERR_INVALID_ARGUMENT, "4-byte aligned"),
     (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARGUMENT, "finite"),
+    (dict(Nk=1 << 24, d=128), fa.FA_ERR_UNSUPPORTED, "2^31 bytes"),
 ])
 def test_fp8_forward_argument_errors(args, status, needle):
     call = dict(FP8)
