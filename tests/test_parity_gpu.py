@@ -2,8 +2,8 @@
 
 Sizes span several tiles and ragged tails; the five named workloads run at full size (the
 16K causal prefill compares sampled rows, every head). Edge cases: single key, empty sequences,
-Nk == 0, poisoned padding, huge scores, negative and zero scale, bitwise repeatability, and
-decode (split-KV) against the tiled kernel.
+Nk == 0, poisoned padding, huge scores, negative and zero scale, bitwise repeatability,
+decode (split-KV) against the tiled kernel, and the largest head the entry points accept.
 """
 
 import numpy as np
@@ -269,3 +269,32 @@ def test_runs_on_a_side_stream():
     s.synchronize()
     o_ref, lse_ref = run_oracle(q, k, v, scale, True, None)
     compare(to_f64(o), to_f64(lse), o_ref, lse_ref, "bf16", what="side stream")
+
+
+def test_largest_head_prefill_and_decode():
+    """K and V at the largest head the entry points accept, 2^31 - 256 bytes (8388607 keys at
+    d = 128): buffer offsets reach the top of their 32-bit range. One ragged length just below it,
+    non-causal; the 8-wave kernel (2100 rows), the 4-wave kernel (300 rows) and the split-KV
+    decode (1 row) on the same keys, each against the oracle on sampled rows."""
+    d = 128
+    nk = (1 << 31) // (2 * d) - 1
+    q = _rand((1, 1, 2100, d), 401, "bf16")
+    k = _rand((1, 1, nk, d), 402, "bf16")
+    v = _rand((1, 1, nk, d), 403, "bf16")
+    lt = torch.tensor([nk - 5], dtype=torch.int32, device=DEV)
+    scale = d ** -0.5
+    rows = np.array([0, 1, 299, 1023, 2047, 2048, 2099])
+    o_ref, lse_ref = run_oracle(q, k, v, scale, False, lt, rows=rows)
+    for nq in (2100, 300, 1):
+        qs = q[:, :, :nq].contiguous()
+        o, lse = run_lib(qs, k, v, scale, False, lt)
+        sel = rows < nq
+        rt = torch.as_tensor(rows[sel], device=DEV)
+        og, lg = to_f64(o[:, :, rt]), to_f64(lse[:, :, rt])
+        compare(og, lg, o_ref[:, :, sel], lse_ref[:, :, sel], "bf16", what=f"Nk={nk} Nq={nq}")
+        rel = np.linalg.norm(og - o_ref[:, :, sel]) / np.linalg.norm(o_ref[:, :, sel])
+        assert rel < 1e-2, f"Nq={nq}: relative Frobenius error {rel:.3e}"
+    with pytest.raises(fa.FaError) as ei:
+        fa.attention(q[:, :, :1].contiguous(), torch.cat([k, k[:, :, :1]], dim=2),
+                     torch.cat([v, v[:, :, :1]], dim=2), scale=scale)
+    assert ei.value.status == fa.FA_ERR_UNSUPPORTED
