@@ -193,8 +193,12 @@ def attention_backward(q, k, v, o, lse, dout, scale: Optional[float] = None, cau
 
     B, H, Nq, Nk, d = _check_qkv(q, k, v, kv_seqlens, (torch.bfloat16,))
     for t in (o, dout):
-        if t.dtype != torch.bfloat16 or tuple(t.shape) != (B, H, Nq, d) or not t.is_contiguous():
-            raise ValueError("o and dout must be contiguous bf16 [B, H, Nq, d]")
+        if (t.dtype != torch.bfloat16 or tuple(t.shape) != (B, H, Nq, d) or not t.is_contiguous()
+                or t.device != q.device):
+            raise ValueError("o and dout must be contiguous bf16 [B, H, Nq, d] on q's device")
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise ValueError("lse must be the forward's contiguous float32 [B, H, Nq] on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -219,17 +223,14 @@ def varlen_attention(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous bfloat16 device tensors")
     for c in (cu_seqlens_q, cu_seqlens_k):
-        if c.dtype != torch.int32 or not c.is_cuda:
-            raise ValueError("cu_seqlens must be int32 device tensors")
+        if c.dtype != torch.int32 or not c.is_cuda or not c.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous int32 device tensors")
     B = cu_seqlens_q.numel() - 1
     if B < 0 or cu_seqlens_k.numel() != B + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B + 1 entries")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
+    out, lse = _out_lse(out, lse, (H, Tq, d), q.dtype, (H, Tq), q.device)
     fa_fwd_varlen(q, k, v, out, lse, B, H, Tq, Tk, max_seqlen_q, d, scale, window[0], window[1],
                   cu_seqlens_q, cu_seqlens_k, stream)
     return out, lse
@@ -286,8 +287,8 @@ def quantize_fp8(x, kv_seqlens=None, transpose: bool = False, stream=None):
         raise ValueError("x must be a contiguous bfloat16 device tensor [B, H, N, d]")
     B, H, N, d = x.shape
     if kv_seqlens is not None and (kv_seqlens.dtype != torch.int32 or not kv_seqlens.is_cuda
-                                   or kv_seqlens.numel() != B):
-        raise ValueError("kv_seqlens must be an int32 device tensor of length B")
+                                   or kv_seqlens.numel() != B or not kv_seqlens.is_contiguous()):
+        raise ValueError("kv_seqlens must be a contiguous int32 device tensor of length B")
     shape = (B, H, d, fa_fp8_vt_cols(N)) if transpose else (B, H, N, d)
     y = torch.empty(shape, dtype=torch.uint8, device=x.device)
     descale = torch.empty((B, H), dtype=torch.float32, device=x.device)
@@ -311,19 +312,35 @@ def attention_fp8(q8, k8, vt8, descale_q, descale_k, descale_v, scale: Optional[
         if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("q8, k8, vt8 must be contiguous uint8 device tensors")
     for t in (descale_q, descale_k, descale_v):
-        if t is not None and (t.dtype != torch.float32 or t.numel() != B * H or not t.is_cuda):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != B * H or not t.is_cuda
+                              or not t.is_contiguous()):
             raise ValueError("descales must be fp32 device tensors of B*H entries (or None)")
     if kv_seqlens is not None and (kv_seqlens.dtype != torch.int32 or not kv_seqlens.is_cuda
-                                   or kv_seqlens.numel() != B):
-        raise ValueError("kv_seqlens must be an int32 device tensor of length B")
+                                   or kv_seqlens.numel() != B or not kv_seqlens.is_contiguous()):
+        raise ValueError("kv_seqlens must be a contiguous int32 device tensor of length B")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q8.device)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device)
+    out, lse = _out_lse(out, lse, (B, H, Nq, d), torch.bfloat16, (B, H, Nq), q8.device)
     fa_fwd_fp8(q8, k8, vt8, descale_q, descale_k, descale_v, out, lse, B, H, Nq, Nk, d, scale,
                int(bool(causal)), kv_seqlens, stream)
+    return out, lse
+
+
+def _out_lse(out, lse, o_shape, o_dtype, l_shape, device):
+    """The caller's O and lse tensors, checked (the kernels write exactly these shapes, so a smaller
+    or strided buffer would be written past its end), or new ones."""
+    import torch
+
+    if out is None:
+        out = torch.empty(o_shape, dtype=o_dtype, device=device)
+    elif (tuple(out.shape) != tuple(o_shape) or out.dtype != o_dtype or out.device != device
+          or not out.is_contiguous()):
+        raise ValueError(f"out must be a contiguous {o_dtype} tensor of shape {tuple(o_shape)} on {device}")
+    if lse is None:
+        lse = torch.empty(l_shape, dtype=torch.float32, device=device)
+    elif (tuple(lse.shape) != tuple(l_shape) or lse.dtype != torch.float32 or lse.device != device
+          or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {tuple(l_shape)} on {device}")
     return out, lse
 
 
@@ -339,11 +356,12 @@ def _check_qkv(q, k, v, kv_seqlens, dtypes):
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in dtypes:
         raise ValueError("q, k, v must share one of the dtypes " + ", ".join(map(str, dtypes)))
     for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous device tensors")
+        if not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous tensors on one device")
     if kv_seqlens is not None:
-        if kv_seqlens.dtype != torch.int32 or not kv_seqlens.is_cuda or kv_seqlens.numel() != B:
-            raise ValueError("kv_seqlens must be an int32 device tensor of length B")
+        if (kv_seqlens.dtype != torch.int32 or kv_seqlens.device != q.device or kv_seqlens.numel() != B
+                or not kv_seqlens.is_contiguous()):
+            raise ValueError("kv_seqlens must be a contiguous int32 tensor of length B on q's device")
     return B, H, Nq, Nk, d
 
 
@@ -356,10 +374,7 @@ def standard_attention(q, k, v, scale: Optional[float] = None, causal: bool = Fa
     B, H, Nq, Nk, d = _check_qkv(q, k, v, kv_seqlens, (torch.bfloat16,))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    out, lse = _out_lse(out, lse, q.shape, q.dtype, (B, H, Nq), q.device)
     need = fa_std_workspace_bytes(B, H, Nq, Nk)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -379,10 +394,7 @@ def attention(q, k, v, scale: Optional[float] = None, causal: bool = False, kv_s
     B, H, Nq, Nk, d = _check_qkv(q, k, v, kv_seqlens, (torch.bfloat16, torch.float32))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    out, lse = _out_lse(out, lse, q.shape, q.dtype, (B, H, Nq), q.device)
     if window is not None:
         if causal or q.dtype != torch.bfloat16:
             raise ValueError("window needs bf16 inputs and causal=False (use window (-1, 0))")

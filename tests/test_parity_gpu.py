@@ -298,3 +298,30 @@ def test_largest_head_prefill_and_decode():
         fa.attention(q[:, :, :1].contiguous(), torch.cat([k, k[:, :, :1]], dim=2),
                      torch.cat([v, v[:, :, :1]], dim=2), scale=scale)
     assert ei.value.status == fa.FA_ERR_UNSUPPORTED
+
+
+def test_bindings_reject_buffers_the_kernels_would_overrun():
+    """Caller-supplied O, lse and length tensors are checked before any launch: a smaller, strided
+    or mistyped buffer raises instead of being written past its end."""
+    q, k, v, _, scale = _case(2, 2, 70, 70, 64, "bf16", False, None, seed=111)
+    good_o, good_l = torch.empty_like(q), torch.empty((2, 2, 70), dtype=torch.float32, device=DEV)
+    bad = [
+        dict(out=torch.empty((2, 2, 69, 64), dtype=torch.bfloat16, device=DEV)),
+        dict(out=torch.empty((2, 2, 64, 70), dtype=torch.bfloat16, device=DEV).transpose(2, 3)),
+        dict(out=torch.empty_like(q, dtype=torch.float32)),
+        dict(lse=torch.empty((2, 2, 70), dtype=torch.bfloat16, device=DEV)),
+        dict(lse=torch.empty((2, 70), dtype=torch.float32, device=DEV)),
+        dict(kv_seqlens=torch.tensor([70, 0, 70, 0], dtype=torch.int32, device=DEV)[::2]),
+    ]
+    for kw in bad:
+        args = dict(out=good_o, lse=good_l, kv_seqlens=None)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            fa.attention(q, k, v, scale=scale, **args)
+    o, lse = fa.attention(q, k, v, scale=scale, out=good_o, lse=good_l)
+    assert o.data_ptr() == good_o.data_ptr() and lse.data_ptr() == good_l.data_ptr()
+    with pytest.raises(ValueError):
+        fa.attention_backward(q, k, v, o, lse[:, :1], torch.empty_like(q), scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = run_oracle(q, k, v, scale, False, None)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, "bf16", what="caller buffers")
