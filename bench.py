@@ -407,6 +407,9 @@ def main():
               "(batch, head) shards with no communication: each GPU would run fa_fwd on its own "
               "batches or heads.", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
 
     import torch
     import io_aware_exact_23_amd as fa

@@ -22,6 +22,14 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert "one GPU only" in r.stderr and r.stdout == ""
 
 
+@pytest.mark.parametrize("flags", [["--steps", "0"], ["--warmup", "-1"]])
+def test_step_counts_are_checked(flags):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *flags],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--steps must be >= 1" in r.stderr and r.stdout == ""
+
+
 def test_counted_flops_of_the_workloads():
     # 4*B*H*Nq*Nk*d, halved when causal.
     assert configs.LONG_CAUSAL_16K.counted_flops() == 2 * 16 * 16384 * 16384 * 128 * 2
