@@ -117,7 +117,9 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  *   [B][H][Nq] fa_fwd wrote for the same inputs, scale, mask and lengths. Arguments as for fa_fwd
  *   (any Nq). bf16 products on the matrix cores with fp32 accumulation; P and dS rounded to bf16
  *   before their products; gradients rounded to bf16 once. Deterministic (no atomics). A
- *   workspace of 4*B*H*Nq bytes is allocated and freed stream-ordered on `stream`.
+ *   workspace of 4*B*H*Nq bytes is allocated and freed stream-ordered on `stream`. With Nq == 0
+ *   and B*H*Nk > 0, dk and dv are written as zeros, and k, v, dk and dv must then be valid
+ *   (non-null, 16-byte aligned).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d,

@@ -193,9 +193,12 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
     // No query rows: dK and dV are still defined, zero, when there are keys (the dK/dV kernel
     // writes them without visiting any query tile; the other kernels have no rows to run on).
     if ((int64_t)B * H > 0 && Nk > 0 && Nq == 0) {
-      if (!dk || !dv) return fail(FA_ERR_INVALID_ARGUMENT, "dk and dv must be non-null");
-      if (!aligned(dk, 16) || !aligned(dv, 16))
-        return fail(FA_ERR_INVALID_ARGUMENT, "dout, dq, dk and dv must be 16-byte aligned");
+      // The kernel still reads K and V (it loads its keys before finding no query tile).
+      if (!k || !v || !dk || !dv) return fail(FA_ERR_INVALID_ARGUMENT, "k, v, dk and dv must be non-null");
+      if (!aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+        return fail(FA_ERR_INVALID_ARGUMENT, "k, v, dk and dv must be 16-byte aligned");
+      if (kv_seqlens && !aligned(kv_seqlens, 4))
+        return fail(FA_ERR_INVALID_ARGUMENT, "lse and kv_seqlens must be 4-byte aligned");
       fa::BackwardParams p{};
       p.dk = dk;
       p.dv = dv;

@@ -222,6 +222,9 @@ BWD = dict(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, dk=A, dv=A, B=2, H=3, Nq=8, 
     (dict(dout=A + 8), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
     (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARGUMENT, "finite"),
     (dict(Nq=0, dk=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(Nq=0, k=None), fa.FA_ERR_INVALID_ARGUMENT, "non-null"),
+    (dict(Nq=0, v=A + 8), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(Nq=0, kv_seqlens=A + 2), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
     (dict(Nq=1 << 24, d=64), fa.FA_ERR_UNSUPPORTED, "2^31 bytes"),
 ])
 def test_backward_argument_errors(args, status, needle):
