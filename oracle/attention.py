@@ -52,6 +52,11 @@ rule of the definition above, for an upstream gradient dO, materialising P:
   dV = P^T dO,   dP = dO V^T,   D_i = sum_j P_ij dP_ij  (= dO_i . O_i),
   dS_ij = P_ij (dP_ij - D_i),   dQ = scale * dS K,   dK = scale * dS^T Q;
 masked pairs have P_ij = 0 and so contribute nothing; rows with no allowed key get dQ_i = 0.
+
+Key slots at or past L_b are outside every allowed set; the oracle slices them off before any
+product (forward and backward), so whatever they hold -- NaN and Inf included -- cannot reach a
+result, and their key and value gradients are zero. Invalid positions must stay out of the
+computation altogether ([dataflow] section "精度、掩码和边界情况").
 """
 
 from __future__ import annotations
@@ -98,17 +103,20 @@ def attention_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.nd
     """The definition for one (batch, head) and a set of query rows.
 
     q_rows: (R, d) fp64, the query vectors of the rows listed in ``rows`` (their indices i).
-    k, v:   (Nk, d) fp64.
-    Returns O (R, d), lse (R,) and, when asked, P (R, Nk).
+    k, v:   (Nk, d) fp64; only rows below ``length`` are read.
+    Returns O (R, d), lse (R,) and, when asked, P (R, Nk) (zero at and past ``length``).
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    nk = k.shape[0]
-    ok = allowed_mask(rows, nk, length, causal, window)
+    nk = np.shape(k)[0]
+    # Key slots at or past the length are outside every allowed set and are never read: they
+    # may hold anything (NaN, Inf), so they are cut off before any arithmetic touches them.
+    length = int(min(max(int(length), 0), nk))
+    k = np.asarray(k, dtype=np.float64)[:length]
+    v = np.asarray(v, dtype=np.float64)[:length]
+    ok = allowed_mask(rows, length, length, causal, window)
 
     # S = scale * Q K^T, with masked entries at -inf (they never enter the normalisation).
-    s = np.full((len(rows), nk), -np.inf)
+    s = np.full((len(rows), length), -np.inf)
     dots = q_rows @ k.T
     s[ok] = float(scale) * dots[ok]
 
@@ -125,7 +133,9 @@ def attention_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.nd
     lse[has_key] = m[has_key] + np.log(l[has_key])
     o[~has_key] = 0.0
     if return_p:
-        return o, lse, p
+        p_full = np.zeros((len(rows), nk))
+        p_full[:, :length] = p
+        return o, lse, p_full
     return o, lse
 
 
@@ -187,12 +197,15 @@ def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, s
     for b in range(bsz):
         length = _length(kv_seqlens, b, nk)
         for h in range(heads):
-            _, _, p = attention_rows(q[b, h], k[b, h], v[b, h], rows, scale, causal, length,
+            # Only the key slots below the length enter any product; the gradients of the
+            # slots past it stay zero.
+            kb, vb = k[b, h, :length], v[b, h, :length]
+            _, _, p = attention_rows(q[b, h], kb, vb, rows, scale, causal, length,
                                      return_p=True, window=window)
-            dv[b, h] = p.T @ do[b, h]
-            dp = do[b, h] @ v[b, h].T
+            dv[b, h, :length] = p.T @ do[b, h]
+            dp = do[b, h] @ vb.T
             d_i = np.sum(p * dp, axis=1)
             ds = p * (dp - d_i[:, None])
-            dq[b, h] = float(scale) * (ds @ k[b, h])
-            dk[b, h] = float(scale) * (ds.T @ q[b, h])
+            dq[b, h] = float(scale) * (ds @ kb)
+            dk[b, h, :length] = float(scale) * (ds.T @ q[b, h])
     return dq, dk, dv

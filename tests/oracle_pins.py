@@ -12,7 +12,9 @@ AssertionError when the implementation disagrees with:
 * invariants: rows of P sum to 1, masked keys get exactly zero weight, permuting keys with
   their values changes nothing, shifting every key by t leaves O unchanged and moves lse by
   scale * q.t;
-* stability: scores of magnitude ~1000 stay finite and exact.
+* stability: scores of magnitude ~1000 stay finite and exact;
+* the padding contract: NaN, Inf or huge values in key slots at or past L_b leave every output
+  bit-identical to zero padding (those slots never enter a product).
 
 The same pins run against deliberately broken copies of the oracle (tests/test_oracle_mutants.py)
 to show that a plausible mistake fails at least one of them.
@@ -220,9 +222,49 @@ def pin_large_scores(impl):
     _close(lse, lse_ref, 1e-12, "large scores lse")
 
 
+def poison_padding(x, lens, fill):
+    """Copy of x (B, H, N, d) whose slots at or past each sequence's length hold ``fill``
+    (a scalar or an array broadcast over those slots)."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    n = y.shape[2]
+    for b in range(y.shape[0]):
+        length = n if lens is None else min(max(int(lens[b]), 0), n)
+        y[b, :, length:] = fill
+    return y
+
+
+# Key and value paddings that a product touching them could not survive: NaN, both infinities,
+# and huge finite values whose products overflow.
+POISONS = ((np.nan, np.inf), (np.inf, np.nan), (-np.inf, -np.inf), (1e308, -1e308))
+
+
+def pin_poisoned_padding(impl):
+    """Key slots at or past L_b are outside every allowed set, so whatever they hold must leave
+    O and lse bit-identical to zero padding: the slots must never enter a product."""
+    cases = [
+        # (B, H, Nq, Nk, d, causal, lens, seed)
+        (4, 2, 4, 5, 3, False, [3, 5, 0, 1], 41),
+        (2, 1, 6, 6, 2, True, [4, 6], 42),
+        (1, 1, 3, 9, 4, False, [2], 43),
+    ]
+    for bsz, heads, nq, nk, d, causal, lens, seed in cases:
+        r = _rng(seed)
+        q = r.standard_normal((bsz, heads, nq, d))
+        k = poison_padding(r.standard_normal((bsz, heads, nk, d)), lens, 0.0)
+        v = poison_padding(r.standard_normal((bsz, heads, nk, d + 1)), lens, 0.0)
+        o_ref, lse_ref = impl(q, k, v, 0.9, causal, lens)
+        for kfill, vfill in POISONS:
+            with np.errstate(all="ignore"):
+                o, lse = impl(q, poison_padding(k, lens, kfill), poison_padding(v, lens, vfill),
+                              0.9, causal, lens)
+            assert np.all(np.isfinite(o)), f"poisoned padding ({kfill}, {vfill}) reached O"
+            assert np.array_equal(o, o_ref), f"poisoned padding ({kfill}, {vfill}) changed O"
+            assert np.array_equal(lse, lse_ref), f"poisoned padding ({kfill}, {vfill}) changed lse"
+
+
 ALL_PINS = [pin_brute_force, pin_golden, pin_zero_query_is_mean, pin_single_key, pin_constant_v,
             pin_causal_first_row, pin_probabilities, pin_key_permutation, pin_key_shift,
-            pin_large_scores]
+            pin_large_scores, pin_poisoned_padding]
 
 
 # ---- sliding windows: impl(q, k, v, scale, causal=False, kv_seqlens=None, return_p=False,
@@ -415,7 +457,31 @@ def pin_bwd_key_shift_sums(impl, fwd):
         _close(dk.sum(axis=2), np.zeros((2, 2, 4)), 1e-13, "sum_j dK_j = 0")
 
 
-BWD_PINS = [pin_bwd_finite_differences, pin_bwd_single_key, pin_bwd_uniform, pin_bwd_key_shift_sums]
+def pin_bwd_poisoned_padding(impl, fwd):
+    """Poisoned key slots past L_b leave dQ, dK and dV bit-identical to zero padding, and those
+    slots get exactly zero gradient."""
+    for bsz, heads, nq, nk, d, causal, lens, seed in ((3, 2, 4, 6, 3, False, [2, 6, 0], 44),
+                                                      (2, 1, 5, 5, 2, True, [3, 5], 45)):
+        r = _rng(seed)
+        q = r.standard_normal((bsz, heads, nq, d))
+        k = poison_padding(r.standard_normal((bsz, heads, nk, d)), lens, 0.0)
+        v = poison_padding(r.standard_normal((bsz, heads, nk, d + 1)), lens, 0.0)
+        do = r.standard_normal((bsz, heads, nq, d + 1))
+        ref = impl(q, k, v, do, 0.8, causal, lens)
+        for b, length in enumerate(lens):
+            assert np.all(ref[1][b, :, length:] == 0.0) and np.all(ref[2][b, :, length:] == 0.0), \
+                "slots past the length get zero key and value gradients"
+        for kfill, vfill in POISONS:
+            with np.errstate(all="ignore"):
+                got = impl(q, poison_padding(k, lens, kfill), poison_padding(v, lens, vfill), do,
+                           0.8, causal, lens)
+            for name, g, g_ref in zip("qkv", got, ref):
+                assert np.all(np.isfinite(g)), f"poisoned padding ({kfill}, {vfill}) reached d{name}"
+                assert np.array_equal(g, g_ref), f"poisoned padding ({kfill}, {vfill}) changed d{name}"
+
+
+BWD_PINS = [pin_bwd_finite_differences, pin_bwd_single_key, pin_bwd_uniform, pin_bwd_key_shift_sums,
+            pin_bwd_poisoned_padding]
 
 
 # ---- FP8 (e4m3) path. Each pin takes a namespace ``f`` with the oracle's functions: decode,

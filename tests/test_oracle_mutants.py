@@ -31,10 +31,16 @@ def make_mutant(kind):
                 ok = np.broadcast_to(j < L, (nq, nk)).copy()
                 if causal:
                     ok &= (j < i) if kind == "causal_strict" else (j <= i)
+                # Only the slots below the length are read, unless the mutant multiplies its zero
+                # weights through the padding.
+                kk = k[b, h] if kind == "padding_multiplied" else k[b, h, :L]
+                vv = v[b, h] if kind == "padding_multiplied" else v[b, h, :L]
+                ok = ok[:, : kk.shape[0]]
                 sc = 1.0 if kind == "no_scale" else scale
-                s = np.where(ok, sc * (q[b, h] @ k[b, h].T), -np.inf)
+                with np.errstate(invalid="ignore", over="ignore"):
+                    s = np.where(ok, sc * (q[b, h] @ kk.T), -np.inf)
                 has = ok.any(axis=1)
-                m = np.where(has, s.max(axis=1), 0.0)
+                m = np.where(has, s.max(axis=1, initial=-np.inf), 0.0)
                 if kind == "no_shift":
                     m = np.zeros_like(m)
                 with np.errstate(over="ignore", invalid="ignore"):
@@ -51,15 +57,17 @@ def make_mutant(kind):
                     else:
                         l = e.sum(axis=1)
                         p = e if kind == "no_normalise" else np.where(has[:, None], e / np.where(l > 0, l, 1.0)[:, None], 0.0)
-                if kind == "transposed_pv" and nq == nk:
-                    out = p.T @ v[b, h]
+                if kind == "transposed_pv" and nq == vv.shape[0]:
+                    out = p.T @ vv
                 else:
-                    out = p @ v[b, h]
+                    with np.errstate(invalid="ignore", over="ignore"):
+                        out = p @ vv
                 out[~has] = 0.0
                 with np.errstate(divide="ignore"):
                     lv = np.log(l) if kind == "lse_no_max" else m + np.log(l)
                 lv = np.where(has, lv, -np.inf)
-                o[b, h], lse[b, h], pp[b, h] = out, lv, p
+                o[b, h], lse[b, h] = out, lv
+                pp[b, h, :, : p.shape[1]] = p
         if return_p:
             return o, lse, pp
         return o, lse
@@ -67,7 +75,8 @@ def make_mutant(kind):
 
 
 MUTANTS = ["no_scale", "causal_strict", "padding_ignored", "padding_off_by_one", "no_shift",
-           "shift_sign", "softmax_wrong_axis", "no_normalise", "lse_no_max", "transposed_pv"]
+           "shift_sign", "softmax_wrong_axis", "no_normalise", "lse_no_max", "transposed_pv",
+           "padding_multiplied"]
 
 
 @pytest.mark.parametrize("kind", MUTANTS)
@@ -168,25 +177,32 @@ def make_bwd_mutant(kind):
         bsz, heads, nq, _ = q.shape
         dq = np.zeros_like(q); dk = np.zeros_like(k); dv = np.zeros_like(v)
         _, _, p_all = _fwd(q, k, v, scale, causal, kv_seqlens, return_p=True, window=window)
+        nk = k.shape[2]
         for b in range(bsz):
+            L = nk if kv_seqlens is None else min(max(int(kv_seqlens[b]), 0), nk)
+            if kind == "padding_multiplied":
+                L = nk  # zero weights multiplied through the padded slots
             for h in range(heads):
-                p = p_all[b, h]
-                dv[b, h] = (p @ do[b, h][: p.shape[1]] if kind == "dv_not_transposed" and p.shape[0] == p.shape[1]
-                            else p.T @ do[b, h])
-                dp = do[b, h] @ v[b, h].T
-                d_i = np.sum(p * dp, axis=1)
-                ds = p * dp if kind == "no_row_term" else p * (dp - d_i[:, None])
-                sq = 1.0 if kind == "dq_no_scale" else scale
-                dq[b, h] = sq * (ds @ k[b, h])
-                dk[b, h] = scale * (ds @ q[b, h] if kind == "dk_not_transposed" and ds.shape[0] == ds.shape[1]
-                                    else ds.T @ q[b, h])
+                p = p_all[b, h, :, :L]
+                kk, vv = k[b, h, :L], v[b, h, :L]
+                dv[b, h, :L] = (p @ do[b, h][: p.shape[1]] if kind == "dv_not_transposed" and p.shape[0] == p.shape[1]
+                                else p.T @ do[b, h])
+                with np.errstate(invalid="ignore", over="ignore"):
+                    dp = do[b, h] @ vv.T
+                    d_i = np.sum(p * dp, axis=1)
+                    ds = p * dp if kind == "no_row_term" else p * (dp - d_i[:, None])
+                    sq = 1.0 if kind == "dq_no_scale" else scale
+                    dq[b, h] = sq * (ds @ kk)
+                    dk[b, h, :L] = scale * (ds @ q[b, h] if kind == "dk_not_transposed" and ds.shape[0] == ds.shape[1]
+                                            else ds.T @ q[b, h])
                 if kind == "dk_sign":
                     dk[b, h] = -dk[b, h]
         return dq, dk, dv
     return impl
 
 
-BWD_MUTANTS = ["dv_not_transposed", "no_row_term", "dq_no_scale", "dk_not_transposed", "dk_sign"]
+BWD_MUTANTS = ["dv_not_transposed", "no_row_term", "dq_no_scale", "dk_not_transposed", "dk_sign",
+               "padding_multiplied"]
 
 
 @pytest.mark.parametrize("kind", BWD_MUTANTS)
