@@ -7,8 +7,14 @@ decode workload (B=64, H=32, Nk=8192 cache with valid lengths in [1024, 8192], d
 the same run and reported under "decode". Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode]
-                  [--no-standard] [--no-masks] [--no-backward] [--no-fp8] [--no-cpu-baseline]
-                  [--cpu-seconds S] [--calibrate-copy]
+                  [--no-short] [--no-standard] [--no-masks] [--no-backward] [--no-fp8]
+                  [--no-cpu-baseline] [--cpu-seconds S] [--calibrate-copy]
+
+"run" records the GPU, its peak engine clock, the ROCm, HIP and hipcc versions and the host CPU.
+"cpu_baseline" is the fp64 oracle timed on a bounded sample of the workload on the host cores;
+"parity" compares the GPU output of the last timed step with the oracle on the same rows.
+"short_prefill" times the GPT-2- and BERT-shaped workloads per launch from a replayed HIP graph
+(no host launch gaps) with their MFMA roofline objects.
 
 The standard (materialising) algorithm, fa_std_fwd, is timed on the three prefill workloads and
 reported under "standard_attention" with its speedup ratio against fa_fwd (the pages' headline
@@ -42,6 +48,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s (bf16) and % of MFMA peak; decode HBM GB/s"
 PEAK_MFMA_BF16_TFLOPS = 2516.6   # MI355X dense bf16: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_MFMA_FP8_TFLOPS = 5033.2    # MI355X dense fp8: 256 CU x 2.4 GHz x 8192 FLOP/clk
+PEAK_MFMA_FP32_TFLOPS = 157.3    # MI355X dense fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 # Sources each profiled kernel is built from: a committed counter summary counts for the current
 # build only if the hash of its kernel's sources matches.
@@ -108,12 +115,70 @@ def time_launches(fn, steps: int, warmup: int, torch):
     return total, per
 
 
-def cpu_baseline_prefill(w, q, k, v, seconds: float):
-    """The oracle, untuned, on a bounded sample of the workload.
+def host_identity() -> dict:
+    """The host CPU the oracle baseline runs on: model name, logical cores, cores this process may
+    use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "logical_cores": os.cpu_count(), "usable_cores": usable}
+
+
+def run_identity(torch) -> dict:
+    """GPU, software versions and host of this run, so that every figure traces to one record."""
+    import ctypes
+    import subprocess
+
+    props = torch.cuda.get_device_properties(0)
+    ident = {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+             "compute_units": props.multi_processor_count, "hbm_bytes": props.total_memory,
+             "torch": torch.__version__, "torch_hip": torch.version.hip}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate (= 5 in hip_runtime_api.h): peak engine clock in kHz.
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, torch.cuda.current_device()) == 0:
+            ident["peak_sclk_mhz"] = val.value / 1000.0
+    except OSError:
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            ident["rocm"] = f.read().strip()
+    except OSError:
+        ident["rocm"] = None
+    try:
+        r = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=60)
+        lines = [ln.strip() for ln in r.stdout.splitlines() if ln.strip()]
+        ident["hipcc"] = "; ".join(lines[:2]) if lines else None
+    except (OSError, subprocess.TimeoutExpired):
+        ident["hipcc"] = None
+    ident["host"] = host_identity()
+    return ident
+
+
+# O and lse tolerances of the bf16 path against the fp64 oracle (max-abs, mean-abs, lse max-abs).
+BF16_TOL = (2e-2, 2e-3, 1e-3)
+FP32_TOL = (1e-5, 1e-5, 1e-3)
+
+
+def cpu_baseline_prefill(w, q, k, v, o, lse, seconds: float):
+    """The oracle, untuned, on a bounded sample of the workload; its rows are also compared with the
+    GPU output of the timed run (o, lse), so the rate comes with the error on the same rows.
 
     Heads are taken in order (b, h) = (0, 0), (0, 1), ...; each head's query rows are visited in
     16 interleaved passes (rows r, r+16, r+32, ...), so every pass has the same mix of causal
-    row lengths. Sampling stops after the first pass that ends past `seconds`.
+    row lengths. Sampling stops after the first pass that ends past `seconds`. Only the oracle
+    calls are timed.
     """
     import threadpoolctl
     from oracle import attention_fwd
@@ -122,34 +187,57 @@ def cpu_baseline_prefill(w, q, k, v, seconds: float):
     flops = 0
     rows_done = 0
     heads = []
-    t0 = time.perf_counter()
+    t_oracle = 0.0
+    err_max = err_sum = lse_max = 0.0
+    n_elem = 0
     done = False
     for b in range(w.B):
         for h in range(w.H):
             qh = q[b:b + 1, h:h + 1].float().cpu().double().numpy()
             kh = k[b:b + 1, h:h + 1].float().cpu().double().numpy()
             vh = v[b:b + 1, h:h + 1].float().cpu().double().numpy()
+            og = o[b, h].float().cpu().double().numpy()
+            lg = lse[b, h].cpu().double().numpy()
             heads.append((b, h))
             for start in range(stride):
                 rows = np.arange(start, w.Nq, stride)
-                attention_fwd(qh, kh, vh, w.scale, causal=w.causal, rows=rows)
+                t0 = time.perf_counter()
+                o_ref, lse_ref = attention_fwd(qh, kh, vh, w.scale, causal=w.causal, rows=rows)
+                t_oracle += time.perf_counter() - t0
+                e = np.abs(og[rows] - o_ref[0, 0])
+                err_max = max(err_max, float(e.max()))
+                err_sum += float(e.sum())
+                n_elem += e.size
+                fin = np.isfinite(lse_ref[0, 0])
+                if fin.any():
+                    lse_max = max(lse_max, float(np.abs(lg[rows][fin] - lse_ref[0, 0][fin]).max()))
                 # Same counting convention as the GPU: 4*d per (query, allowed key) pair.
                 n_keys = (rows + 1) if w.causal else np.full(len(rows), w.Nk)
                 flops += int(4 * w.d * n_keys.sum())
                 rows_done += len(rows)
-                if time.perf_counter() - t0 >= seconds:
+                if t_oracle >= seconds:
                     done = True
                     break
             if done:
                 break
         if done:
             break
-    dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows_done} query rows ({len(heads)} heads, from (b, h) = (0, 0) in order) of "
-                      f"{w.name}, fp64 numpy with {threads} BLAS threads, {dt:.1f} s; FLOPs counted "
-                      f"as 4*d per (query row, allowed key)"}
+    host = host_identity()
+    base = {"value": flops / t_oracle / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "blas_threads": threads, "host_logical_cores": host["logical_cores"],
+            "host_usable_cores": host["usable_cores"], "host_cpu_model": host["cpu_model"],
+            "sample": f"{rows_done} of {w.B * w.H * w.Nq} query rows ({len(heads)} heads, from (b, h) = (0, 0) "
+                      f"in order, each head's rows in 16 interleaved passes) of {w.name}: fp64 numpy with "
+                      f"{threads} BLAS threads, {t_oracle:.1f} s of oracle time; the value is the rate over this "
+                      f"sample, FLOPs counted as 4*d per (query row, allowed key)"}
+    mx, mn, lt = BF16_TOL if w.dtype == "bf16" else FP32_TOL
+    parity = {"rows_compared": rows_done, "heads": len(heads), "o_max_abs": err_max,
+              "o_mean_abs": err_sum / max(n_elem, 1), "lse_max_abs": lse_max,
+              "tolerance": {"o_max_abs": mx, "o_mean_abs": mn, "lse_max_abs": lt},
+              "what": "GPU output of the last timed step against the fp64 oracle on the cpu_baseline rows"}
+    parity["within_tolerance"] = bool(err_max <= mx and parity["o_mean_abs"] <= mn and lse_max <= lt)
+    return base, parity
 
 
 def allowed_scores(w, lens) -> int:
@@ -375,6 +463,70 @@ def bench_fp8(fa, configs, inputs, torch, dev, steps, warmup):
     return out
 
 
+def graph_time_per_launch(fn, launches: int, replays: int, warmup: int, torch) -> float:
+    """Seconds per launch of fn, measured with HIP events around replays of a HIP graph holding
+    `launches` back-to-back calls: the device-side time of the kernels with no host launch gaps,
+    which otherwise dominate launches of a few tens of microseconds. fn must launch kernels only
+    (no allocation, no memset)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(max(warmup, 1)):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(launches):
+            fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(replays):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) / 1e3 / (launches * replays)
+
+
+def bench_short_prefill(fa, configs, inputs, torch, dev, warmup):
+    """The short prefill workloads (GPT-2 and BERT shapes, prefill_bf16_kernel) timed per launch
+    without host gaps (graph replay), each with its MFMA roofline object."""
+    out = []
+    for name in PREFILL_WORKLOADS[:2]:
+        w = configs.BY_NAME[name]
+        q, k, v, lens = inputs.make(w, dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+
+        def run():
+            fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal), lens, None)
+
+        per = graph_time_per_launch(run, 50, 10, warmup, torch)
+        fl = w.counted_flops()
+        rec = {"workload": name, "kernel_ms": round(per * 1e3, 5), "counted_flops": fl,
+               "roofline": {"kernel": "prefill_bf16_kernel", "bound": "mfma",
+                            "achieved": round(fl / per / 1e12, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(fl / per / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
+                            "avg_launch_ms": round(per * 1e3, 5),
+                            "timing": "HIP events around 10 replays of a graph of 50 launches",
+                            "traffic": traffic_from_profile("prefill_bf16_kernel", name,
+                                                            source_sha("prefill_bf16_kernel")),
+                            "source_sha": source_sha("prefill_bf16_kernel")}}
+        if lens is not None:
+            pairs = allowed_scores(w, lens.cpu().numpy())
+            rec["allowed_pair_flops"] = 4 * w.d * pairs
+            rec["TFLOPs_allowed_pairs"] = round(4 * w.d * pairs / per / 1e12, 1)
+        out.append(rec)
+        del q, k, v, o, lse
+    return out
+
+
 def decode_bytes(w, lens) -> int:
     per_key = 2 * w.d * 2                      # one K row and one V row, bf16
     per_bh = 2 * w.d * 2 + 4                   # Q and O rows (bf16) and lse (fp32)
@@ -396,6 +548,8 @@ def main():
                     help="skip the backward-pass timing (fa_bwd)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the e4m3 forward timing (fa_quantize_fp8, fa_fwd_fp8)")
+    ap.add_argument("--no-short", action="store_true",
+                    help="skip the graph-replayed timing of the short prefill workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -434,10 +588,27 @@ def main():
     value = flops * args.steps / total / 1e12
     avg_launch = float(np.mean(per))
     achieved = flops / avg_launch / 1e12
-    if w.Nq == 1:
-        kernel = "decode_split_kernel"
+    if w.dtype == "fp32":
+        kernel, peak = "prefill_f32_kernel", PEAK_MFMA_FP32_TFLOPS
+    elif w.Nq == 1:
+        kernel, peak = "decode_split_kernel", PEAK_MFMA_BF16_TFLOPS
     else:
         kernel = "prefill_bf16_pp_kernel" if w.Nq >= LONG_NQ else "prefill_bf16_kernel"
+        peak = PEAK_MFMA_BF16_TFLOPS
+    sha = source_sha(kernel) if kernel in KERNEL_SOURCES else None
+    if w.Nq == 1 and w.dtype == "bf16":
+        # A decode main workload is bound by HBM: its roofline is bytes, not FLOPs.
+        nbytes = decode_bytes(w, (lens.cpu().numpy() if lens is not None else np.full(w.B, w.Nk)))
+        roof = {"kernel": "decode_split_kernel + decode_combine_kernel (whole call)", "bound": "hbm",
+                "achieved": round(nbytes / avg_launch / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(nbytes / avg_launch / 1e9 / PEAK_HBM_GBS, 4),
+                "avg_launch_ms": round(avg_launch * 1e3, 4),
+                "traffic": traffic_from_profile(kernel, w.name, sha), "source_sha": sha}
+    else:
+        roof = {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "avg_launch_ms": round(avg_launch * 1e3, 4),
+                "traffic": traffic_from_profile(kernel, w.name, sha) if sha else None, "source_sha": sha}
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -454,13 +625,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal, "input_std": w.input_std, "seed": w.seed,
                    "counted_flops": flops},
-        "pct_mfma_peak": round(100.0 * value / PEAK_MFMA_BF16_TFLOPS, 2),
-        "roofline": {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4),
-                     "avg_launch_ms": round(avg_launch * 1e3, 4),
-                     "traffic": traffic_from_profile(kernel, w.name, source_sha(kernel)),
-                     "source_sha": source_sha(kernel)},
+        "pct_mfma_peak": round(100.0 * value / peak, 2),
+        "roofline": roof,
+        "run": run_identity(torch),
     }
 
     if not args.no_decode:
@@ -491,6 +658,9 @@ def main():
         }
         del dq, dk, dv, do
 
+    if not args.no_short:
+        result["short_prefill"] = bench_short_prefill(fa, configs, inputs, torch, dev, args.warmup)
+
     if not args.no_masks:
         result["masks"] = bench_masks(fa, configs, inputs, torch, dev, args.steps, args.warmup)
 
@@ -515,7 +685,7 @@ def main():
         result["calibration_copy_bytes"] = src.numel() * 2
 
     if not args.no_cpu_baseline and w.Nq > 1:
-        result["cpu_baseline"] = cpu_baseline_prefill(w, q, k, v, args.cpu_seconds)
+        result["cpu_baseline"], result["parity"] = cpu_baseline_prefill(w, q, k, v, o, lse, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
 

@@ -56,6 +56,11 @@ typedef enum {
  *   if set, Nq == Nk. B*H*Nq == 0 is a valid no-op; Nk == 0 gives O = 0 and lse = -inf.
  *   Nq == 1 runs the split-KV decode kernels (one query per (b, h)); any other Nq runs the
  *   tiled prefill kernel.
+ *   Decode splits each sequence's keys into chunks of 128 and combines the chunks' partial
+ *   (o, lse) by their logsumexp; the combine is exact for any chunk size, so results agree across
+ *   it to fp32 rounding. The environment variable FA_DECODE_CHUNK (64, 128 or 256), read once per
+ *   process, overrides the chunk size; any other value makes every Nq == 1 call return
+ *   FA_ERR_INVALID_ARGUMENT.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Nq, int Nk, int d, float scale, int causal,

@@ -6,6 +6,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <limits>
 
 #include "fa.h"
@@ -16,7 +18,7 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream
 hipError_t launch_prefill_bf16_pp(const PrefillParams& p, int d, hipStream_t stream);
 hipError_t launch_prefill_bf16_general(const PrefillParams& p, int d, int max_nq, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream);
-hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams& p, int d, int chunk, hipStream_t stream);
 hipError_t launch_standard(const StandardParams& p, int d, hipStream_t stream);
 hipError_t launch_backward(const BackwardParams& p, int d, hipStream_t stream);
 hipError_t launch_quantize_fp8(const QuantParams& p, hipStream_t stream);
@@ -25,7 +27,6 @@ int prefill_fp8_rows_per_wg();
 int prefill_bf16_rows_per_wg(int d);
 int prefill_bf16_pp_rows_per_wg();
 constexpr int kPrefillLongNq = 2048;  // query rows from which the 8-wave prefill kernel is used
-int decode_chunk();
 }  // namespace fa
 
 namespace {
@@ -70,6 +71,22 @@ int check_common(const void* q, const void* k, const void* v, const void* o, con
   if (!aligned(lse, 4) || (kv_seqlens && !aligned(kv_seqlens, 4)))
     return fail(FA_ERR_INVALID_ARGUMENT, "lse and kv_seqlens must be 4-byte aligned");
   return FA_OK;
+}
+
+// Keys per split of the decode path: 128, unless the environment variable FA_DECODE_CHUNK, read
+// once per process, names 64 or 256 (the split size is free: the combine is exact for any size,
+// so this exists to check that results agree across it). Any other value makes every decode call
+// fail rather than silently run another size.
+int decode_chunk_keys() {
+  static const int chunk = [] {
+    const char* s = std::getenv("FA_DECODE_CHUNK");
+    if (s == nullptr || *s == '\0') return 128;
+    if (std::strcmp(s, "64") == 0) return 64;
+    if (std::strcmp(s, "128") == 0) return 128;
+    if (std::strcmp(s, "256") == 0) return 256;
+    return -1;
+  }();
+  return chunk;
 }
 
 // Compute units per XCD of the current device (the MI355X has 8 XCDs), 0 when the count is not a
@@ -138,7 +155,8 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
     p.H = H;
     p.Nk = Nk;
     p.c = (float)((double)scale * 1.4426950408889634);
-    const int chunk = fa::decode_chunk();
+    const int chunk = decode_chunk_keys();
+    if (chunk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "FA_DECODE_CHUNK must be 64, 128 or 256");
     p.n_splits = (Nk + chunk - 1) / chunk;
     const size_t n_part = (size_t)B * H * (size_t)p.n_splits;
     void* ws = nullptr;
@@ -148,7 +166,7 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
       p.ws_o = static_cast<float*>(ws);
       p.ws_lse = p.ws_o + n_part * d;
     }
-    hipError_t e = fa::launch_decode_bf16(p, d, s);
+    hipError_t e = fa::launch_decode_bf16(p, d, chunk, s);
     if (ws) {
       hipError_t ef = hipFreeAsync(ws, s);
       if (e == hipSuccess) e = ef;

@@ -5,7 +5,7 @@
 // FlashDecoding as its IO-aware form (section "結論"). With one query there is no reuse of K/V,
 // so the pass is bound by HBM bandwidth: every valid key is read exactly once.
 //
-// Kernel 1 (split): one workgroup per (chunk of kDecodeChunk keys, h, b). Each wave streams
+// Kernel 1 (split): one workgroup per (chunk of CHUNK keys, h, b). Each wave streams
 // kDecodeKeysPerWave keys with 16-byte non-temporal loads (the keys are read once: keeping them in the caches only
 // evicts what other workgroups still need; +5.5% on the decode workload), kLanesPerKey lanes
 // per key row (whole rows per load instruction: perfectly coalesced), forms the dot products on
@@ -23,10 +23,10 @@ namespace fa {
 // Keys per chunk and per wave. Measured on the decode workload (64 x 32 heads, up to 8192 keys),
 // whole call: 128-key chunks of 4 waves x 32 keys 5.94 TB/s; of 2 waves x 64 keys 5.89 (with 8 x 16
 // the same); 256-key chunks 5.7, 512-key chunks 4.4; 96-key chunks 5.77, 64-key chunks 5.4-5.5,
-// where the partial outputs and their combine cost more than the finer balance gains.
-constexpr int kDecodeChunk = 128;
+// where the partial outputs and their combine cost more than the finer balance gains. 128 is the
+// default; 64 and 256 are built too, since the split size is free (the combine is exact for any
+// chunk size) and the results must agree across it to fp32 rounding.
 constexpr int kDecodeKeysPerWave = 32;
-constexpr int kDecodeThreads = 64 * kDecodeChunk / kDecodeKeysPerWave;
 
 // Sum over aligned groups of N lanes (N a power of two <= 64).
 template <int N>
@@ -215,17 +215,25 @@ void decode_combine_kernel(DecodeParams p) {
   if (lane == 0) p.lse[bh] = n > 0 ? (M + fast_log2(W)) * kLn2 : -kInf;
 }
 
-int decode_chunk() { return kDecodeChunk; }
+template <int D, int CHUNK>
+void launch_decode(const DecodeParams& p, hipStream_t stream) {
+  constexpr int kThreads = 64 * CHUNK / kDecodeKeysPerWave;
+  if (p.n_splits > 0)
+    hipLaunchKernelGGL((decode_split_kernel<D, CHUNK>), dim3(p.n_splits, p.H, p.B), dim3(kThreads), 0,
+                       stream, p);
+  hipLaunchKernelGGL((decode_combine_kernel<D, CHUNK>), dim3(p.B * p.H), dim3(64), 0, stream, p);
+}
 
-hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream) {
-  const dim3 grid1(p.n_splits, p.H, p.B);
-  const dim3 grid2(p.B * p.H);
+// chunk: keys per split, 64, 128 or 256 (p.n_splits = ceil(Nk / chunk)); the caller checks it.
+hipError_t launch_decode_bf16(const DecodeParams& p, int d, int chunk, hipStream_t stream) {
   if (d == 64) {
-    if (p.n_splits > 0) hipLaunchKernelGGL((decode_split_kernel<64, kDecodeChunk>), grid1, dim3(kDecodeThreads), 0, stream, p);
-    hipLaunchKernelGGL((decode_combine_kernel<64, kDecodeChunk>), grid2, dim3(64), 0, stream, p);
+    if (chunk == 64) launch_decode<64, 64>(p, stream);
+    else if (chunk == 256) launch_decode<64, 256>(p, stream);
+    else launch_decode<64, 128>(p, stream);
   } else {
-    if (p.n_splits > 0) hipLaunchKernelGGL((decode_split_kernel<128, kDecodeChunk>), grid1, dim3(kDecodeThreads), 0, stream, p);
-    hipLaunchKernelGGL((decode_combine_kernel<128, kDecodeChunk>), grid2, dim3(64), 0, stream, p);
+    if (chunk == 64) launch_decode<128, 64>(p, stream);
+    else if (chunk == 256) launch_decode<128, 256>(p, stream);
+    else launch_decode<128, 128>(p, stream);
   }
   return hipGetLastError();
 }

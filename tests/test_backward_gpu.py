@@ -87,6 +87,41 @@ def test_backward_keys_past_length_get_zero_gradient():
     assert torch.all(dk[2, :, 37:] == 0) and torch.all(dv[2, :, 37:] == 0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_poisoned_padding_against_oracle(d):
+    """NaN / Inf in the key and value slots at or past L_b: the gradients must match the oracle's
+    (which never reads those slots), be bit-identical to those with zero padding, and be zero for
+    the padded slots."""
+    B, H, Nq, Nk = 3, 2, 200, 300
+    lens = [300, 45, 0]
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    q, k, v = _rand((B, H, Nq, d), 5 + d), _rand((B, H, Nk, d), 6 + d), _rand((B, H, Nk, d), 7 + d)
+    do = _rand((B, H, Nq, d), 8 + d)
+    inputs.fill_padding(k, lt.cpu(), 0.0)
+    inputs.fill_padding(v, lt.cpu(), 0.0)
+    scale = d ** -0.5
+
+    def grads(kk, vv):
+        o, lse = fa.attention(q, kk, vv, scale=scale, kv_seqlens=lt)
+        g = fa.attention_backward(q, kk, vv, o, lse, do, scale=scale, kv_seqlens=lt)
+        torch.cuda.synchronize()
+        return g
+
+    clean = grads(k, v)
+    for kfill, vfill in ((float("nan"), float("inf")), (float("-inf"), float("nan"))):
+        kp, vp = k.clone(), v.clone()
+        inputs.fill_padding(kp, lt.cpu(), kfill)
+        inputs.fill_padding(vp, lt.cpu(), vfill)
+        got = grads(kp, vp)
+        ref = attention_bwd(to_f64(q), to_f64(kp), to_f64(vp), to_f64(do), f32(scale), kv_seqlens=lens)
+        tag = f"poisoned ({kfill}, {vfill}) d={d}"
+        for name, g, c, r in zip(("dQ", "dK", "dV"), got, clean, ref):
+            _grad_close(to_f64(g), r, f"{name} {tag}")
+            assert torch.equal(g.view(torch.int16), c.view(torch.int16)), f"{name} {tag}"
+        for b, n in enumerate(lens):
+            assert torch.all(got[1][b, :, n:] == 0) and torch.all(got[2][b, :, n:] == 0)
+
+
 def test_backward_large_scores():
     run_case(1, 2, 300, 300, 64, True, None, seed=11, std=3.0, scale=0.5, what="large scores")
 

@@ -310,3 +310,33 @@ def test_quantize_empty_batch_and_vt_cols():
     fa.fa_quantize_fp8(**call)
     assert fa.fa_last_error() == ""
     assert [fa.fa_fp8_vt_cols(n) for n in (0, 1, 63, 64, 65, 16384)] == [0, 64, 64, 64, 128, 16384]
+
+
+@needs_lib
+@pytest.mark.parametrize("value", ["100", "512", "abc"])
+def test_decode_chunk_override_rejects_other_values(value):
+    """FA_DECODE_CHUNK is read once per process, so each value runs in a fresh interpreter; a value
+    other than 64, 128 or 256 makes a decode call (Nq == 1) fail before anything is launched, while
+    prefill calls are unaffected by it."""
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import io_aware_exact_23_amd as fa\n"
+        "A = 0x10000000\n"
+        "try:\n"
+        "    fa.fa_fwd(q=A, k=A, v=A, o=A, lse=A, B=2, H=3, Nq=1, Nk=8, d=64, scale=0.1, causal=0,\n"
+        "              kv_seqlens=None, stream=0)\n"
+        "except fa.FaError as e:\n"
+        "    print(e.status, e.message)\n"
+        "try:\n"
+        "    fa.fa_fwd(q=A, k=A, v=A, o=A, lse=A, B=2, H=3, Nq=4, Nk=8, d=96, scale=0.1, causal=0,\n"
+        "              kv_seqlens=None, stream=0)\n"
+        "except fa.FaError as e:\n"
+        "    print(e.status, e.message)\n" % ROOT)
+    env = dict(os.environ, FA_DECODE_CHUNK=value)
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = r.stdout.strip().splitlines()
+    assert lines[0].startswith(f"{fa.FA_ERR_INVALID_ARGUMENT} ") and "FA_DECODE_CHUNK" in lines[0]
+    assert lines[1].startswith(f"{fa.FA_ERR_UNSUPPORTED} ") and "64 or 128" in lines[1]

@@ -62,6 +62,28 @@ def test_window(B, H, N, d, window, lens):
     compare(to_f64(o), to_f64(lse), o_ref, lse_ref, "bf16", what=f"window {window} N={N}")
 
 
+@pytest.mark.parametrize("window", [(255, 0), (100, 100), (-1, -1)])
+def test_window_poisoned_padding_against_oracle(window):
+    """NaN in the key slots and Inf in the value slots at or past L_b, under sliding windows: the
+    output must match the oracle (which never reads those slots) and equal the zero-padded run bit
+    for bit."""
+    B, H, N, d = 2, 2, 2100, 128
+    lens = [2100, 1333]
+    lt = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    q, k, v = (_rand((B, H, N, d), 300 + s) for s in range(3))
+    inputs.fill_padding(k, lt.cpu(), 0.0)
+    inputs.fill_padding(v, lt.cpu(), 0.0)
+    o1, l1 = fa.attention(q, k, v, scale=d ** -0.5, kv_seqlens=lt, window=window)
+    kp, vp = k.clone(), v.clone()
+    inputs.fill_padding(kp, lt.cpu(), float("nan"))
+    inputs.fill_padding(vp, lt.cpu(), float("inf"))
+    o2, l2 = fa.attention(q, kp, vp, scale=d ** -0.5, kv_seqlens=lt, window=window)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = run_oracle(q, kp, vp, d ** -0.5, False, lt, window=window)
+    compare(to_f64(o2), to_f64(l2), o_ref, lse_ref, "bf16", what=f"poisoned window {window}")
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
 def test_window_reductions_match_fa_fwd():
     # (-1, 0) is the causal mask and (-1, -1) no mask: the general kernel against fa_fwd's.
     q, k, v = (_rand((2, 2, 2048, 128), 90 + s) for s in range(3))
