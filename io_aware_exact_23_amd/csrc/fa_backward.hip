@@ -33,30 +33,8 @@
 
 namespace fa {
 
-// Row of a 32-row block read by accumulator row r (an involution: swap bits 2 and 3).
-__device__ __forceinline__ int bwd_perm(int r) {
-  return (r & ~0xC) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2);
-}
-
-template <int N>
-__device__ __forceinline__ void bwd_wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
-}
-
-// Workgroup barrier that waits only for this wave's LDS accesses (lgkmcnt 0, vmcnt untouched):
-// __syncthreads() would also drain every vector-memory load in flight, including the next tile's
-// copies, and so serialise the prefetch. A wave waits for its own tile copies explicitly before
-// the barrier that publishes them. The empty asm keeps the compiler from moving memory accesses
-// across the barrier.
-__device__ __forceinline__ void bwd_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt 63 (no wait), expcnt 7, lgkmcnt 0
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-}
+// Row of a 32-row block read by accumulator row r: key_row_perm (bits 2 and 3 swapped).
+__device__ __forceinline__ int bwd_perm(int r) { return key_row_perm(r); }
 
 // ---- D_i = dO_i . O_i (fp32). D/8 lanes share a row, 16 bytes of O and of dO each, so one wave
 // load covers 64/(D/8) whole rows; each lane takes kRowSteps rows, all loads issued before the
@@ -228,7 +206,7 @@ void bwd_dq_kernel(BackwardParams p) {
   }
   // Wait for the register loads once and hide their origin, so the loop carries no vector-memory
   // waits for them (such waits would also drain the tile copies in flight).
-  bwd_wait_vmcnt<0>();
+  wait_vmcnt<0>();
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(qd[ks]));
   asm volatile("" : "+v"(lsd));
@@ -405,23 +383,23 @@ void bwd_dq_kernel(BackwardParams p) {
     if (swave) __builtin_amdgcn_s_setprio(1);
     phase_a(stage_tag, t * 64);
     __builtin_amdgcn_s_setprio(0);
-    bwd_barrier();
+    wg_barrier_lds();
     phase_b(stage_tag);
-    if (more) bwd_wait_vmcnt<0>();
-    bwd_barrier();
+    if (more) wait_vmcnt<0>();
+    wg_barrier_lds();
   };
 
   if (ntiles > 0) {
     issue(0, 0);
-    bwd_wait_vmcnt<0>();
+    wait_vmcnt<0>();
   }
-  bwd_barrier();
+  wg_barrier_lds();
   for (int t = 0; t < ntiles; t += 2) {
     interval(std::integral_constant<int, 0>{}, t);
     if (t + 1 >= ntiles) break;
     interval(std::integral_constant<int, 1>{}, t + 1);
   }
-  bwd_wait_vmcnt<0>();
+  wait_vmcnt<0>();
 
   // The two waves of a pair hold the sums over their own keys for the whole head dimension. Each
   // writes the half the partner stores into the stage area (no longer read: the loop's last
@@ -540,7 +518,7 @@ void bwd_dkdv_kernel(BackwardParams p) {
   // Wait for these loads once, then hide their origin: otherwise the loop's matrix instructions
   // carry conservative vector-memory waits that also drain the next tile's copies issued just
   // before them, serialising the prefetch.
-  bwd_wait_vmcnt<0>();
+  wait_vmcnt<0>();
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+v"(kv[ks]));
   const float c = p.scale * kLog2e;
@@ -761,18 +739,18 @@ void bwd_dkdv_kernel(BackwardParams p) {
     if (pwave) __builtin_amdgcn_s_setprio(1);
     phase_a(stage_tag, t);
     __builtin_amdgcn_s_setprio(0);
-    bwd_barrier();
+    wg_barrier_lds();
     phase_b(stage_tag);
     if (more) {
-      bwd_wait_vmcnt<0>();
+      wait_vmcnt<0>();
       publish(1 - S);
     }
-    bwd_barrier();
+    wg_barrier_lds();
   };
 
   if (t0 < tn) {
     issue(t0, 0);
-    bwd_wait_vmcnt<0>();
+    wait_vmcnt<0>();
     publish(0);
   }
   __syncthreads();
@@ -781,7 +759,7 @@ void bwd_dkdv_kernel(BackwardParams p) {
     if (t + 1 >= tn) break;
     interval(std::integral_constant<int, 1>{}, t + 1);
   }
-  bwd_wait_vmcnt<0>();
+  wait_vmcnt<0>();
 
   if (kj < p.Nk) {
     uint16_t* outg = static_cast<uint16_t*>(pwave ? p.dv : p.dk) + (size_t)bh * p.Nk * D + (size_t)kj * D;

@@ -87,6 +87,51 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
+// s_waitcnt immediates in the gfx9 encoding that gfx950 uses: vmcnt in bits 3:0 and 15:14, expcnt
+// in bits 6:4, lgkmcnt (LDS, scalar memory) in bits 11:8. A field at its maximum (63, 7, 15) does
+// not wait on that counter.
+constexpr int waitcnt_imm(int vmcnt, int expcnt, int lgkmcnt) {
+  return (vmcnt & 15) | ((vmcnt >> 4) << 14) | ((expcnt & 7) << 4) | ((lgkmcnt & 15) << 8);
+}
+constexpr int kWaitLdsOnly = waitcnt_imm(63, 7, 0);  // this wave's LDS accesses, nothing else
+
+// Wait until at most N of this wave's vector-memory operations are outstanding (loads complete in
+// order, so the older ones have landed), leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, 7, 15));
+}
+
+// Workgroup barrier with no memory wait of its own; the scheduling barriers keep the compiler from
+// moving instructions across it.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup barrier that waits only for this wave's LDS accesses (lgkmcnt 0, vmcnt untouched):
+// __syncthreads() would also drain every vector-memory load in flight, including the next tile's
+// copies, and so serialise the prefetch. A wave waits for its own tile copies explicitly before
+// the barrier that publishes them. The empty asm keeps the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void wg_barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Row permutation of a 32-key block held in LDS (an involution: bits 2 and 3 swapped). With K rows
+// stored in this order, the 16 scores a lane holds in the accumulator of a 32x32 S^T = K Q^T block
+// are two runs of 8 consecutive keys, so each run is one 16-byte read of the transposed V tile.
+__device__ __forceinline__ int key_row_perm(int r) {
+  return (r & ~0xC) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2);
+}
+
 // Workgroups of one launch are handed out round-robin over the 8 XCDs of the MI355X, and each
 // XCD has its own L2. Map hardware workgroup id -> logical tile so that every XCD receives one
 // contiguous range of logical tiles (tiles that share K/V then share an L2).

@@ -48,10 +48,6 @@ struct PrefillBf16Cfg {
   static_assert(kKiBPerWave * kWaves * 1024 == kTileBytes, "tile must split over the waves");
 };
 
-// Row of the K tile in LDS that holds key `r` of the tile (an involution: swap bits 2 and 3).
-__device__ __forceinline__ int k_perm(int r) {
-  return (r & ~0xC) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2);
-}
 
 // WPE waves per SIMD, i.e. WPE workgroups per CU. At d = 64 a wave needs about 150 VGPRs and a
 // workgroup 32 KB of LDS, so three fit: with one wave per workgroup on each SIMD, the matrix work
@@ -131,7 +127,7 @@ void prefill_bf16_kernel(PrefillParams p) {
   }
 
   // ---- HBM -> LDS. Wave w moves KiB blocks w*kKiBPerWave .. of each tile; in a block, lane i
-  // fills LDS row rb + i/kNch, 16-byte slot i%kNch. A K row r holds key k_perm(r) with piece
+  // fills LDS row rb + i/kNch, 16-byte slot i%kNch. A K row r holds key key_row_perm(r) with piece
   // (slot ^ kswz(r)); a V row r holds key r with piece (slot ^ vswz(r)). Both spread what one pass
   // of a read serves over all 64 banks. At d = 128 a row fills the 256-byte bank line: kswz(r) =
   // r % 16, vswz(r) = 4 * (r % 4). At d = 64 two rows share a line, so rows of one parity must
@@ -146,7 +142,7 @@ void prefill_bf16_kernel(PrefillParams p) {
   for (int it = 0; it < C::kKiBPerWave; ++it) {
     const int row = (w * C::kKiBPerWave + it) * C::kRowsPerKiB + lane / C::kNch;
     const int slot = lane % C::kNch;
-    koff[it] = (uint32_t)(k_perm(row) * C::kRowBytes + ((slot ^ kswz(row)) << 4));
+    koff[it] = (uint32_t)(key_row_perm(row) * C::kRowBytes + ((slot ^ kswz(row)) << 4));
     voff[it] = (uint32_t)(row * C::kRowBytes + ((slot ^ vswz(row)) << 4));
   }
   auto issue = [&](int j, char* stage) {
@@ -294,7 +290,7 @@ void prefill_bf16_kernel(PrefillParams p) {
       if (need_mask) tile_step(std::true_type{}, cur, k0);
       else tile_step(std::false_type{}, cur, k0);
     }
-    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads have landed in LDS
+    wait_vmcnt<0>();  // this wave's loads have landed in LDS
     __syncthreads();
   };
 
@@ -306,7 +302,7 @@ void prefill_bf16_kernel(PrefillParams p) {
   __builtin_amdgcn_sched_barrier(0);
   if (ntiles > 0) issue(0, stage_a);
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): Q and tile 0
+  wait_vmcnt<0>();  // Q and tile 0
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
   for (int j = 0; j < ntiles; j += 2) {

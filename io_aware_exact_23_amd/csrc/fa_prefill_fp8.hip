@@ -67,17 +67,6 @@ __device__ __forceinline__ int fp8_k_key(int rho) {
   return 32 * g + 16 * kb + 4 * a + b;
 }
 
-template <int N>
-__device__ __forceinline__ void fp8_wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
-}
-
-__device__ __forceinline__ void fp8_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 __device__ __forceinline__ float fp8_vmax3(float a, float b, float c) {
   float r;
@@ -372,8 +361,8 @@ void prefill_fp8_kernel(PrefillFp8Params p) {
       set_prio(0);
       matrix_phase(unit);
     }
-    fp8_wait_vmcnt<2 * C::kLoadsPerUnit>();
-    fp8_barrier();
+    wait_vmcnt<2 * C::kLoadsPerUnit>();
+    wg_barrier();
   };
   // Tiles below i_u1 need no mask for any row of the workgroup (whole, and below q0 when causal);
   // interval n only completes tile n - 1 (its own tile is fully masked).
@@ -403,11 +392,11 @@ void prefill_fp8_kernel(PrefillFp8Params p) {
   issue_unit(1, slot1);
   issue_unit(2, slot2);
   __builtin_amdgcn_sched_barrier(0);
-  fp8_wait_vmcnt<0>();
-  fp8_barrier();
+  wait_vmcnt<0>();
+  wg_barrier();
   if (grp == 0) run(std::true_type{});
   else run(std::false_type{});
-  fp8_wait_vmcnt<0>();
+  wait_vmcnt<0>();
 
   // O = s_v * O^T / l, lse = ln 2 * (m + log2(l) - 3); a row with no allowed key gets 0 and -inf.
   const float lt = pair32_sum(lsum);

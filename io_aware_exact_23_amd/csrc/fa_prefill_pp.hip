@@ -86,23 +86,6 @@ struct PrefillPPCfg {
   static_assert(kKiBPerWave * kWaves * 1024 == kTileBytes, "tile must split over the waves");
 };
 
-// Row of the K tile in LDS that holds key `r` of the tile (an involution: swap bits 2 and 3).
-__device__ __forceinline__ int pp_k_perm(int r) {
-  return (r & ~0xC) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2);
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
-}
-
-__device__ __forceinline__ void wg_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 // kGen = false: the fa_fwd masks (causal, key lengths) on [B][H][N][D] tensors. kGen = true:
 // sliding windows (left, right) and, with cu_q / cu_k, packed sequences; the loop structure gains
@@ -211,7 +194,7 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
   float m_used = -kInf, lsum = 0.0f;
 
   // ---- HBM -> LDS. Wave w moves KiB blocks w*kKiBPerWave .. of each tile; in a block, lane i
-  // fills LDS row rb + i/kNch, 16-byte slot i%kNch. A K row r holds key pp_k_perm(r) with piece
+  // fills LDS row rb + i/kNch, 16-byte slot i%kNch. A K row r holds key key_row_perm(r) with piece
   // (slot ^ kswz(r)); a V row r holds key r with piece (slot ^ vswz(r)). At d = 128 a row fills
   // the 256-byte bank line: kswz(r) = r % 16, vswz(r) = 4 * (r % 4). At d = 64 two rows share a
   // line, and rows of one parity must differ in their pieces: kswz(r) = (r / 2) % 8 for the
@@ -225,7 +208,7 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
   for (int it = 0; it < C::kKiBPerWave; ++it) {
     const int row = (w * C::kKiBPerWave + it) * C::kRowsPerKiB + lane / C::kNch;
     const int slot = lane % C::kNch;
-    koff[it] = (uint32_t)(pp_k_perm(row) * C::kRowBytes + ((slot ^ kswz(row)) << 4));
+    koff[it] = (uint32_t)(key_row_perm(row) * C::kRowBytes + ((slot ^ kswz(row)) << 4));
     voff[it] = (uint32_t)(row * C::kRowBytes + ((slot ^ vswz(row)) << 4));
   }
   // Unit u = (K tile i_lo + u, V tile i_lo + u - 1), offsets relative to the views' start. V tile

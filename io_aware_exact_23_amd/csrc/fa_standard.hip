@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void std_scores_kernel(StandardParams p) {
     for (int ks = 0; ks < D / 16; ++ks)
       qa[rb][ks] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (qrow * D + ks * 16 + g * 8) * 2));
   }
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // this wave's K pieces have landed
+  wait_vmcnt<0>();  // this wave's K pieces have landed
   __syncthreads();
 
   float* Sg = p.s + (size_t)bh * p.Nq * p.ld;
@@ -303,12 +303,6 @@ struct StdPvCfg {
   static_assert(kKiBPerWave * kWaves * 1024 == kTileBytes, "tile must split over the waves");
 };
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding, N < 64).
-template <int N>
-__device__ __forceinline__ void std_wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
-}
 
 template <int D>
 __global__ __launch_bounds__(256) void std_pv_kernel(StandardParams p) {
@@ -400,9 +394,9 @@ __global__ __launch_bounds__(256) void std_pv_kernel(StandardParams p) {
     if (more) {
       issue_v(t + 1, stage_b);
       load_p(t + 1, pa[1]);
-      std_wait_vmcnt<C::kKiBPerWave + C::kSteps>();  // tile t landed
+      wait_vmcnt<C::kKiBPerWave + C::kSteps>();  // tile t landed
     } else {
-      std_wait_vmcnt<0>();
+      wait_vmcnt<0>();
     }
     __syncthreads();
     step(stage_a, pa[0]);
@@ -412,9 +406,9 @@ __global__ __launch_bounds__(256) void std_pv_kernel(StandardParams p) {
     if (more2) {
       issue_v(t + 2, stage_a);
       load_p(t + 2, pa[0]);
-      std_wait_vmcnt<C::kKiBPerWave + C::kSteps>();  // tile t+1 landed
+      wait_vmcnt<C::kKiBPerWave + C::kSteps>();  // tile t+1 landed
     } else {
-      std_wait_vmcnt<0>();
+      wait_vmcnt<0>();
     }
     __syncthreads();
     step(stage_b, pa[1]);

@@ -395,8 +395,8 @@ def test_decode_split_size_invariance(tmp_path):
     size. The decode workload (B 64, H 32, Nk 8192, d 128, ragged lengths) runs with 64-, 128- and
     256-key chunks, each in its own process (the library reads FA_DECODE_CHUNK once per process),
     one after the other. lse must agree across chunk sizes within 1e-6 relative; O, rounded to
-    bf16 once from fp32 values that agree to that level, within one bf16 unit in the last place;
-    and every run must match the oracle."""
+    bf16 once from fp32 values that agree to about 2^-20 max|V|, within one bf16 unit in the last
+    place plus that; and every run must match the oracle."""
     import os
     import subprocess
     import sys
@@ -422,14 +422,54 @@ def test_decode_split_size_invariance(tmp_path):
     o_ref, lse_ref = np.concatenate(o_ref_all), np.concatenate(lse_ref_all)
     for chunk, (o, lse) in runs.items():
         compare(o, lse, o_ref, lse_ref, "bf16", what=f"{w.name} chunk {chunk}")
+    # Before its rounding to bf16, O is a weighted mean of V rows accumulated in fp32, so two chunk
+    # sizes agree to about 2^-20 max|V| absolute (O can be much smaller than the V entries it
+    # averages); after rounding they differ by at most that plus one bf16 unit in the last place.
+    vmax = v.float().abs().amax(dim=(2, 3)).cpu().numpy()[:, :, None, None]
     o0, l0 = runs[128]
     for chunk in (64, 256):
         o, lse = runs[chunk]
         dl = np.abs(lse - l0) / np.maximum(1.0, np.abs(l0))
         ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.maximum(np.abs(o), np.abs(o0)), 2.0 ** -126))) - 7)
         do = np.abs(o - o0)
+        lim = ulp + 2.0 ** -20 * vmax
         frac = float(np.mean(do > 0))
+        worst = np.unravel_index(np.argmax(do - lim), do.shape)
         print(f"chunk {chunk} vs 128: lse max rel {dl.max():.2e}, O max {do.max():.2e}, "
-              f"{100 * frac:.3f}% of O elements differ", flush=True)
+              f"{100 * frac:.3f}% of O elements differ; closest to the limit at {tuple(int(x) for x in worst)}: "
+              f"|dO| {do[worst]:.3e} vs {lim[worst]:.3e} (O {o0[worst]:.4e})", flush=True)
         assert dl.max() <= 1e-6, f"chunk {chunk}: lse differs by {dl.max():.3e} relative"
-        assert np.all(do <= ulp), f"chunk {chunk}: O differs by more than one bf16 ulp"
+        assert np.all(do <= lim), f"chunk {chunk}: O differs by more than one bf16 ulp + 2^-20 max|V|"
+
+
+def test_prefill_in_a_replayed_hip_graph_matches_eager():
+    """The benchmark times the short workloads from a replayed HIP graph of fa_fwd launches (the
+    prefill path launches kernels only: no allocation, no memset). Three replays, with eager work
+    and synchronisations between them, each bit-identical to the eager call."""
+    w = configs.GPT2_SMALL_CAUSAL
+    q, k, v, lt = inputs.make(w, DEV)
+    o_e, l_e = run_lib(q, k, v, w.scale, w.causal, lt)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=DEV)
+
+    def launch():
+        fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal), lt, None)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch()
+    for rep in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_e.view(torch.int16)), f"replay {rep}: O differs"
+        assert torch.equal(lse, l_e), f"replay {rep}: lse differs"
+        run_lib(q, k, v, w.scale, w.causal, lt)  # eager work between replays
