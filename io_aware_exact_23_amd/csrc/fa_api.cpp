@@ -324,7 +324,7 @@ extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* 
       (int64_t)total_k * d * 2 > std::numeric_limits<int32_t>::max())
     return fail(FA_ERR_UNSUPPORTED, "one head's packed rows must stay below 2^31 bytes");
   const int bm = fa::prefill_bf16_pp_rows_per_wg();
-  if (bh * ((max_seqlen_q + bm - 1) / bm) > std::numeric_limits<int32_t>::max())
+  if (bh * (((int64_t)max_seqlen_q + bm - 1) / bm) > std::numeric_limits<int32_t>::max())
     return fail(FA_ERR_UNSUPPORTED, "grid too large");
   fa::PrefillParams p = prefill_params(q, k, v, o, lse, B, H, 0, 0, scale, 0, nullptr);
   p.win_left = window_left;

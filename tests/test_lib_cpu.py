@@ -46,6 +46,12 @@ def test_status_strings():
 # Fake device addresses: argument checks must reject these calls before any HIP call.
 A = 0x10000000
 BAD = 0x10000001
+INT_MAX = 2 ** 31 - 1
+
+# The host-sanitizer test (test_host_sanitizers.py) reruns this file against a build of the library
+# whose host code carries AddressSanitizer and UndefinedBehaviorSanitizer checks.
+if os.environ.get("FA_TEST_LIBRARY"):
+    fa._LIB_PATH = os.environ["FA_TEST_LIBRARY"]
 
 
 def _std(**kw):
@@ -88,6 +94,10 @@ ENTRY = {"fa_fwd": lambda **kw: fa.fa_fwd(**kw), "fa_fwd_f32": lambda **kw: fa.f
     (dict(B=70000, H=70000), fa.FA_ERR_UNSUPPORTED, "int32"),
     (dict(Nk=1 << 23, d=128), fa.FA_ERR_UNSUPPORTED, "2^31 bytes"),
     (dict(Nq=1 << 23, Nk=1 << 23, d=128, causal=1), fa.FA_ERR_UNSUPPORTED, "2^31 bytes"),
+    (dict(Nq=INT_MAX, Nk=INT_MAX), fa.FA_ERR_UNSUPPORTED, "2^31 bytes"),
+    (dict(B=INT_MAX, H=INT_MAX), fa.FA_ERR_UNSUPPORTED, "int32"),
+    (dict(B=-INT_MAX - 1), fa.FA_ERR_INVALID_ARGUMENT, ">= 0"),
+    (dict(scale=-float("inf")), fa.FA_ERR_INVALID_ARGUMENT, "finite"),
 ])
 def test_argument_errors(fn, args, status, needle):
     call = dict(q=A, k=A, v=A, o=A, lse=A, B=2, H=3, Nq=8, Nk=8, d=64, scale=0.125, causal=0,
@@ -118,6 +128,7 @@ def test_standard_workspace_errors(args, needle):
 
 @needs_lib
 def test_standard_workspace_size():
+    assert fa.fa_std_workspace_bytes(INT_MAX, INT_MAX, INT_MAX, INT_MAX) == 0  # would not fit in size_t
     assert fa.fa_std_workspace_bytes(2, 3, 8, 8) == 2 * 3 * 8 * 128 * 6
     assert fa.fa_std_workspace_bytes(1, 1, 1, 129) == 256 * 6
     assert fa.fa_std_workspace_bytes(2, 16, 16384, 16384) == 2 * 16 * 16384 * 16384 * 6
@@ -186,6 +197,8 @@ VARLEN = dict(q=A, k=A, v=A, o=A, lse=A, B=2, H=3, total_q=40, total_k=50, max_s
     (dict(q=A + 8), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
     (dict(cu_seqlens_k=A + 2), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
     (dict(total_q=1 << 24), fa.FA_ERR_UNSUPPORTED, "2^31"),
+    (dict(max_seqlen_q=INT_MAX, B=INT_MAX, H=2), fa.FA_ERR_UNSUPPORTED, "grid too large"),
+    (dict(max_seqlen_q=INT_MAX, B=1, H=INT_MAX), fa.FA_ERR_UNSUPPORTED, "grid too large"),
 ])
 def test_varlen_argument_errors(args, status, needle):
     call = dict(VARLEN)
@@ -226,6 +239,8 @@ BWD = dict(q=A, k=A, v=A, o=A, dout=A, lse=A, dq=A, dk=A, dv=A, B=2, H=3, Nq=8, 
     (dict(Nq=0, v=A + 8), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
     (dict(Nq=0, kv_seqlens=A + 2), fa.FA_ERR_INVALID_ARGUMENT, "aligned"),
     (dict(Nq=1 << 24, d=64), fa.FA_ERR_UNSUPPORTED, "2^31 bytes"),
+    (dict(B=INT_MAX, H=INT_MAX), fa.FA_ERR_UNSUPPORTED, "int32"),
+    (dict(Nq=INT_MAX, Nk=1), fa.FA_ERR_UNSUPPORTED, "2^31 bytes"),
 ])
 def test_backward_argument_errors(args, status, needle):
     call = dict(BWD)
@@ -293,6 +308,8 @@ QUANT = dict(x=A, y=A, descale=A, B=2, H=3, N=100, d=128, lens=None, transpose=0
     (dict(y=A + 8), fa.FA_ERR_INVALID_ARGUMENT, "16-byte aligned"),
     (dict(descale=A + 2), fa.FA_ERR_INVALID_ARGUMENT, "4-byte aligned"),
     (dict(N=5000000, transpose=1), fa.FA_ERR_UNSUPPORTED, "transposed"),
+    (dict(N=INT_MAX), fa.FA_ERR_UNSUPPORTED, "2^31"),
+    (dict(B=INT_MAX, H=INT_MAX), fa.FA_ERR_UNSUPPORTED, "int32"),
 ])
 def test_quantize_argument_errors(args, status, needle):
     call = dict(QUANT)
