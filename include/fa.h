@@ -67,6 +67,23 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const int32_t* kv_seqlens, void* stream);
 
 /*
+ * fa_fwd_noalloc -- fa_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): it allocates nothing. The
+ * decode path (Nq == 1) keeps its partial results in a static 72 MiB device array of the library
+ * (each GPU it runs on holds its own copy until the process ends) instead of a stream-ordered
+ * allocation; every other Nq runs exactly what fa_fwd runs, which needs no workspace.
+ *   Same arguments, layouts, arithmetic and results as fa_fwd (bit for bit). Decode calls whose
+ *   partials need more than 72 MiB, 4*(d+1)*B*H*ceil(Nk/128) bytes (a cache of 64 x 32
+ *   sequences x 8192 keys at d = 128 needs 64.5 MiB), return FA_ERR_UNSUPPORTED before anything
+ *   is launched. Every call on one GPU shares that GPU's array: decode calls that overlap on one
+ *   GPU (different streams, or host threads) race and must be ordered by the caller. Nothing in
+ *   the array needs to start at zero.
+ */
+int fa_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                   const int32_t* kv_seqlens, void* stream);
+
+/*
  * fa_fwd_f32 -- the same operation with fp32 q, k, v and o (fp32 products and accumulation on
  * the matrix cores, fp32 softmax). Same argument rules as fa_fwd; every Nq runs the tiled kernel.
  */

@@ -8,6 +8,7 @@ call raises ``FaError``.
 Entry points mirror the C ABI in ``include/fa.h``:
 
 * ``fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, stream)`` -- bf16
+* ``fa_fwd_noalloc(...)`` -- bf16, the same arguments, allocates no device memory
 * ``fa_fwd_f32(...)``                                                          -- fp32
 * ``fa_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, d, scale, window_left, window_right,
   kv_seqlens, stream)`` -- bf16, sliding-window mask
@@ -42,7 +43,7 @@ import math
 import os
 from typing import Optional, Tuple
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_f32", "fa_fwd_window", "fa_fwd_varlen", "fa_bwd",
+__all__ = ["FaError", "fa_fwd", "fa_fwd_noalloc", "fa_fwd_f32", "fa_fwd_window", "fa_fwd_varlen", "fa_bwd",
            "attention_backward", "fa_std_fwd", "fa_quantize_fp8", "fa_fp8_vt_cols", "fa_fwd_fp8",
            "quantize_fp8", "attention_fp8",
            "fa_std_workspace_bytes", "fa_status_string", "fa_last_error", "attention",
@@ -80,7 +81,7 @@ def load_library():
     lib = ctypes.CDLL(_LIB_PATH)
     vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     sig = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp, vp]
-    for name in ("fa_fwd", "fa_fwd_f32"):
+    for name in ("fa_fwd", "fa_fwd_f32", "fa_fwd_noalloc"):
         fn = getattr(lib, name)
         fn.argtypes = sig
         fn.restype = ci
@@ -145,6 +146,12 @@ def _call(name, q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, str
 def fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens=None, stream=None) -> None:
     """bf16 forward; see include/fa.h for the contract."""
     _call("fa_fwd", q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, stream)
+
+
+def fa_fwd_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens=None, stream=None) -> None:
+    """bf16 forward that allocates no device memory (decode partials in the library's static
+    scratch); see include/fa.h for the contract."""
+    _call("fa_fwd_noalloc", q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, stream)
 
 
 def fa_fwd_f32(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens=None, stream=None) -> None:

@@ -19,6 +19,8 @@ hipError_t launch_prefill_bf16_pp(const PrefillParams& p, int d, hipStream_t str
 hipError_t launch_prefill_bf16_general(const PrefillParams& p, int d, int max_nq, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, int chunk, hipStream_t stream);
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_standard(const StandardParams& p, int d, hipStream_t stream);
 hipError_t launch_backward(const BackwardParams& p, int d, hipStream_t stream);
 hipError_t launch_quantize_fp8(const QuantParams& p, hipStream_t stream);
@@ -134,9 +136,14 @@ fa::PrefillParams prefill_params(const void* q, const void* k, const void* v, vo
 
 }  // namespace
 
-extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                      const int32_t* kv_seqlens, void* stream) {
+namespace {
+
+// The bf16 forward behind fa_fwd and fa_fwd_noalloc. Decode (Nq == 1) needs a workspace for its
+// partial results: with noalloc it is the library's static scratch (sizes beyond it are
+// rejected), else a stream-ordered allocation freed after the kernels.
+int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+             int Nk, int d, float scale, int causal, const int32_t* kv_seqlens, void* stream,
+             bool noalloc) {
   int st = check_common(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, 2);
   if (st == 1) return FA_OK;
   if (st != FA_OK) return st;
@@ -159,15 +166,25 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
     if (chunk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "FA_DECODE_CHUNK must be 64, 128 or 256");
     p.n_splits = (Nk + chunk - 1) / chunk;
     const size_t n_part = (size_t)B * H * (size_t)p.n_splits;
+    const size_t ws_bytes = n_part * (size_t)(d + 1) * sizeof(float);
     void* ws = nullptr;
     if (n_part > 0) {
-      hipError_t e = hipMallocAsync(&ws, n_part * (size_t)(d + 1) * sizeof(float), s);
-      if (e != hipSuccess) return fail_hip(e, "hipMallocAsync(decode workspace)");
+      if (noalloc) {
+        if (ws_bytes > fa::decode_scratch_bytes())
+          return fail(FA_ERR_UNSUPPORTED,
+                      "decode partials (4*(d+1)*B*H*ceil(Nk/chunk) bytes) exceed the 72 MiB scratch "
+                      "of fa_fwd_noalloc");
+        hipError_t e = fa::decode_scratch(&ws);
+        if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+      } else {
+        hipError_t e = hipMallocAsync(&ws, ws_bytes, s);
+        if (e != hipSuccess) return fail_hip(e, "hipMallocAsync(decode workspace)");
+      }
       p.ws_o = static_cast<float*>(ws);
       p.ws_lse = p.ws_o + n_part * d;
     }
     hipError_t e = fa::launch_decode_bf16(p, d, chunk, s);
-    if (ws) {
+    if (ws && !noalloc) {
       hipError_t ef = hipFreeAsync(ws, s);
       if (e == hipSuccess) e = ef;
     }
@@ -187,6 +204,20 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
                                           : fa::launch_prefill_bf16(p, d, s);
   if (e != hipSuccess) return fail_hip(e, "prefill launch");
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                      const int32_t* kv_seqlens, void* stream) {
+  return fwd_bf16(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, stream, false);
+}
+
+extern "C" int fa_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                              const int32_t* kv_seqlens, void* stream) {
+  return fwd_bf16(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, stream, true);
 }
 
 extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,

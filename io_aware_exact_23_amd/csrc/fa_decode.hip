@@ -15,10 +15,44 @@
 // Kernel 2 (combine): per (b, h), lse* = max_c lse_c, w_c = 2^(lse_c - lse*),
 // O = sum w_c o_c / sum w_c, lse = ln 2 * (lse* + log2 sum w_c). Exact in exact arithmetic,
 // for any chunk size.
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_params.h"
 
 namespace fa {
+
+// Scratch of the allocation-free entry point (fa_fwd_noalloc): the decode path's partial outputs
+// and logsumexps live here instead of in a stream-ordered allocation. 72 MiB holds the
+// 64 x 32 x ceil(8192 / 128) partials of a cache of 64 sequences x 32 heads x 8192 keys at
+// d = 128 (64.5 MiB). Each GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` is only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, per device (decode_scratch below).
+constexpr size_t kNoAllocScratchBytes = size_t(72) << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+size_t decode_scratch_bytes() { return kNoAllocScratchBytes; }
+
+// Device address of the current device's copy of `scratch`, looked up once per device (with that
+// device current) and kept.
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 // Keys per chunk and per wave. Measured on the decode workload (64 x 32 heads, up to 8192 keys),
 // whole call: 128-key chunks of 4 waves x 32 keys 5.94 TB/s; of 2 waves x 64 keys 5.89 (with 8 x 16

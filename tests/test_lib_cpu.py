@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     assert declared_functions() == ["fa_bwd", "fa_fp8_vt_cols", "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8",
-                                    "fa_fwd_varlen", "fa_fwd_window", "fa_last_error",
+                                    "fa_fwd_noalloc", "fa_fwd_varlen", "fa_fwd_window", "fa_last_error",
                                     "fa_quantize_fp8", "fa_status_string", "fa_std_fwd",
                                     "fa_std_workspace_bytes"]
 
@@ -70,11 +70,12 @@ def _win(**kw):
 
 
 ENTRY = {"fa_fwd": lambda **kw: fa.fa_fwd(**kw), "fa_fwd_f32": lambda **kw: fa.fa_fwd_f32(**kw),
+         "fa_fwd_noalloc": lambda **kw: fa.fa_fwd_noalloc(**kw),
          "fa_std_fwd": _std, "fa_fwd_window": _win}
 
 
 @needs_lib
-@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32", "fa_std_fwd", "fa_fwd_window"])
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32", "fa_std_fwd", "fa_fwd_window", "fa_fwd_noalloc"])
 @pytest.mark.parametrize("args,status,needle", [
     (dict(d=96), fa.FA_ERR_UNSUPPORTED, "64 or 128"),
     (dict(d=0), fa.FA_ERR_UNSUPPORTED, "64 or 128"),
@@ -357,3 +358,19 @@ def test_decode_chunk_override_rejects_other_values(value):
     lines = r.stdout.strip().splitlines()
     assert lines[0].startswith(f"{fa.FA_ERR_INVALID_ARGUMENT} ") and "FA_DECODE_CHUNK" in lines[0]
     assert lines[1].startswith(f"{fa.FA_ERR_UNSUPPORTED} ") and "64 or 128" in lines[1]
+
+
+@needs_lib
+def test_noalloc_rejects_decode_beyond_its_scratch():
+    """fa_fwd_noalloc keeps decode partials in a 72 MiB static array: a call needing more is
+    rejected before any HIP call (fake addresses are never touched)."""
+    # 64 x 32 heads x ceil(16384 / 128) partials x 129 floats = 135 MB > 72 MiB.
+    with pytest.raises(fa.FaError) as ei:
+        fa.fa_fwd_noalloc(q=A, k=A, v=A, o=A, lse=A, B=64, H=32, Nq=1, Nk=16384, d=128, scale=0.1,
+                          causal=0, kv_seqlens=None, stream=0)
+    assert ei.value.status == fa.FA_ERR_UNSUPPORTED and "72 MiB" in ei.value.message
+    # The same argument checks as fa_fwd.
+    with pytest.raises(fa.FaError) as ei:
+        fa.fa_fwd_noalloc(q=A, k=A, v=A, o=A, lse=A, B=2, H=3, Nq=1, Nk=8, d=96, scale=0.1,
+                          causal=0, kv_seqlens=None, stream=0)
+    assert ei.value.status == fa.FA_ERR_UNSUPPORTED
