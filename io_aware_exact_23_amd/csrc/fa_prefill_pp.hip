@@ -104,7 +104,10 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
   const int grp = w >> 2;                                  // waves w and w + 4 share a SIMD
-  const int rblk = 2 * (w & 3) + grp;                      // the wave's 32-row block
+  // The wave's 32-row block: SIMD s holds blocks s and 7 - s, so on the causal diagonal, where
+  // the fully masked 32-key blocks of each wave are skipped, every SIMD keeps the same matrix work
+  // (blocks r and 7 - r need r + 1 and 8 - r of the diagonal's eight key blocks).
+  const int rblk = grp ? 7 - (w & 3) : (w & 3);
   const int r32 = lane & 31;
   const int g = lane >> 5;
 
@@ -324,7 +327,13 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
   // -1 and unit n carries K tile n, both outside the buffer range and read as zeros; P before
   // tile 0 is zero; and a tile with no allowed key for this wave (tile n, tiles past the wave's
   // causal diagonal, rows past Nq) is fully masked, so its P is exactly zero.
-  auto matrix_phase = [&](const char* unit, int hs) __attribute__((always_inline)) {
+  // With kSkip (the masked intervals of fa_fwd), sb and pb are how many leading 32-key blocks of
+  // tile i (S) and of tile i-1 (PV) hold a key allowed for any row of this wave: the products of
+  // the blocks past them are left out (their scores are masked, their P is zero), so causal
+  // diagonal tiles and the closing interval cost only the matrix work they need. The count is
+  // uniform over the wave, so the branches do not diverge.
+  auto matrix_phase = [&](auto skip_tag, const char* unit, int hs, int sb, int pb) __attribute__((always_inline)) {
+    constexpr bool kSkip = decltype(skip_tag)::value;
     const int h = kHi > 0 ? hs : 0;
     const char* Vs = unit + C::kTileBytes;
     auto fetch = [&](int m) -> bf16x8 __attribute__((always_inline)) {
@@ -350,11 +359,13 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
       __builtin_amdgcn_sched_barrier(0);
       if (m + kAhead < kNM) op[m + kAhead] = fetch(m + kAhead);
       if (m < kNS) {
-        sacc[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], qreg[m >> 1], sacc[m & 1], 0, 0, 0);
+        if (!kSkip || (m & 1) < sb)
+          sacc[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], qreg[m >> 1], sacc[m & 1], 0, 0, 0);
       } else {
         const int mp = m - kNS;
         const int db = mp % (D / 32), u = mp / (D / 32);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], pk[u >> 1][u & 1], oacc[db], 0, 0, 0);
+        if (!kSkip || (u >> 1) < pb)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[m], pk[u >> 1][u & 1], oacc[db], 0, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -435,22 +446,34 @@ void prefill_bf16_pp_kernel(PrefillParams p) {
     if (pr) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   };
+  // One past the last key any row of this wave may see (causal diagonal, length, kend), for the
+  // block counts of the masked fa_fwd intervals; rows past Nq see none.
+  const int wave_kend = qw0 >= Nq ? 0 : min(kend, p.causal ? min(qw0 + C::kQW, Nq) : kend);
+  auto blocks_needed = [&](int k0) __attribute__((always_inline)) {
+    return clampi((wave_kend - k0 + 31) >> 5, 0, 2);
+  };
   auto interval = [&](auto order_tag, auto mask_tag, int t, const char* unit, int hs, char* ahead)
       __attribute__((always_inline)) {
     constexpr bool kMatrixFirst = decltype(order_tag)::value;
+    constexpr bool kSkip = !kGen && decltype(mask_tag)::value;
     const int i = i_lo + t;  // key tile of this interval (t counts from the first one)
+    const int sb = kSkip ? blocks_needed(i * C::kBN) : 2;
+    const int pb = kSkip ? blocks_needed((i - 1) * C::kBN) : 2;
     if constexpr (kMatrixFirst) {
-      matrix_phase(unit, hs);
+      matrix_phase(std::integral_constant<bool, kSkip>{}, unit, hs, sb, pb);
       issue_unit(t + 3, ahead);
-      set_prio(1);
-      softmax_phase(mask_tag, i * C::kBN);
-      set_prio(0);
+      // Tile n (the closing interval's own) is fully masked: its softmax would add nothing.
+      if (!kSkip || i < n) {
+        set_prio(1);
+        softmax_phase(mask_tag, i * C::kBN);
+        set_prio(0);
+      }
     } else {
       issue_unit(t + 3, ahead);
       set_prio(1);
       softmax_phase(mask_tag, (i - 1) * C::kBN);
       set_prio(0);
-      matrix_phase(unit, hs);
+      matrix_phase(std::integral_constant<bool, kSkip>{}, unit, hs, sb, pb);
     }
     wait_vmcnt<2 * C::kLoadsPerUnit>();
     wg_barrier();
