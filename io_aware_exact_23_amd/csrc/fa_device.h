@@ -167,4 +167,32 @@ __device__ __forceinline__ bool causal_serpentine(int wg, int n, int nq, int P, 
   return true;
 }
 
+// Padded batches without a causal mask: whole sequences longest first (the longest-processing-time
+// order), so that the workgroups a launch runs after its first wave of resident ones are the
+// lightest. Workgroup wg -> (rank, query tile, head) with rank outermost; the sequence of a rank is
+// found by every lane b < B counting the sequences ordered before sequence b (length descending,
+// then index). Consecutive workgroups are consecutive heads, so with H a multiple of 8 all query
+// tiles of a head land on one XCD (workgroups are dealt to the XCDs round-robin). Needs
+// B <= 64 (one lane per sequence); returns false otherwise.
+__device__ __forceinline__ bool longest_first(int wg, const int32_t* lens, int B, int H, int nq, int nk,
+                                              int& bh, int& qt) {
+  if (lens == nullptr || B > 64) return false;
+  const int lane = threadIdx.x & 63;
+  const int per_rank = H * nq;
+  const int rank = wg / per_rank;
+  const int rest = wg - rank * per_rank;
+  qt = rest / H;
+  const int h = rest - qt * H;
+  const int mylen = lane < B ? seq_len(lens, lane, nk) : -1;
+  int ahead = 0;
+  for (int o = 0; o < B; ++o) {
+    const int lo = __shfl(mylen, o, 64);
+    ahead += (lo > mylen || (lo == mylen && o < lane)) ? 1 : 0;
+  }
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < B && ahead == rank);
+  const int b = __builtin_amdgcn_readfirstlane(hit ? (int)__builtin_ctzll(hit) : 0);
+  bh = b * H + h;
+  return true;
+}
+
 }  // namespace fa

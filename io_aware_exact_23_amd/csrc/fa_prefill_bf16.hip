@@ -68,10 +68,14 @@ void prefill_bf16_kernel(PrefillParams p) {
   const int g = lane >> 5;
 
   // Work decomposition: workgroup -> (b, h, query tile). Causal: tiles of similar total weight
-  // share a CU (serpentine order), or else heaviest first within a head. Otherwise tiles that
-  // share K/V share an XCD.
+  // share a CU (serpentine order), or else heaviest first within a head. Key lengths without a
+  // causal mask: longest sequences first, so the workgroups that run after the first resident
+  // wave of them are the lightest. Otherwise tiles that share K/V share an XCD.
   int bh, qt;
-  if (!(p.causal && causal_serpentine(blockIdx.x, p.n_tiles, p.n_qtiles, p.cus_per_xcd, bh, qt))) {
+  const bool placed = p.causal
+      ? causal_serpentine(blockIdx.x, p.n_tiles, p.n_qtiles, p.cus_per_xcd, bh, qt)
+      : longest_first(blockIdx.x, p.kv_seqlens, p.B, p.H, p.n_qtiles, p.Nk, bh, qt);
+  if (!placed) {
     const int tile = xcd_remap(blockIdx.x, p.n_tiles);
     bh = tile / p.n_qtiles;
     qt = tile - bh * p.n_qtiles;

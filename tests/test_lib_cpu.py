@@ -49,9 +49,8 @@ BAD = 0x10000001
 INT_MAX = 2 ** 31 - 1
 
 # The host-sanitizer test (test_host_sanitizers.py) reruns this file against a build of the library
-# whose host code carries AddressSanitizer and UndefinedBehaviorSanitizer checks.
-if os.environ.get("FA_TEST_LIBRARY"):
-    fa._LIB_PATH = os.environ["FA_TEST_LIBRARY"]
+# whose host code carries AddressSanitizer and UndefinedBehaviorSanitizer checks (FA_TEST_LIBRARY,
+# applied in conftest.py).
 
 
 def _std(**kw):
