@@ -137,7 +137,6 @@ def host_identity() -> dict:
 def run_identity(torch) -> dict:
     """GPU, software versions and host of this run, so that every figure traces to one record."""
     import ctypes
-    import subprocess
 
     props = torch.cuda.get_device_properties(0)
     ident = {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
@@ -157,11 +156,10 @@ def run_identity(torch) -> dict:
     except OSError:
         ident["rocm"] = None
     try:
-        r = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=60)
-        lines = [ln.strip() for ln in r.stdout.splitlines() if ln.strip()]
-        ident["hipcc"] = "; ".join(lines[:2]) if lines else None
-    except (OSError, subprocess.TimeoutExpired):
-        ident["hipcc"] = None
+        import io_aware_exact_23_amd as fa
+        ident["library_build"] = fa.fa_build_info()
+    except (OSError, AttributeError):
+        ident["library_build"] = None
     ident["host"] = host_identity()
     return ident
 

@@ -220,6 +220,10 @@ const char* fa_status_string(int status);
 /* Detail of the last failed call on this host thread ("" if none). */
 const char* fa_last_error(void);
 
+/* Static text naming the compiler and HIP headers the library was built with and its device
+ * target, so a measurement can record what produced the code it timed (never NULL; no GPU call). */
+const char* fa_build_info(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ Entry points mirror the C ABI in ``include/fa.h``:
 * ``fa_fp8_vt_cols(Nk)``
 * ``fa_fwd_fp8(q8, k8, vt8, descale_q, descale_k, descale_v, o, lse, B, H, Nq, Nk, d, scale,
   causal, kv_seqlens, stream)`` -- e4m3 forward
-* ``fa_status_string(status)``, ``fa_last_error()``
+* ``fa_status_string(status)``, ``fa_last_error()``, ``fa_build_info()``
 
 Pointer arguments accept a torch tensor (its ``data_ptr()``), an int address or None; ``stream``
 accepts a ``torch.cuda.Stream``, an int handle or None (the current torch stream).
@@ -46,7 +46,7 @@ from typing import Optional, Tuple
 __all__ = ["FaError", "fa_fwd", "fa_fwd_noalloc", "fa_fwd_f32", "fa_fwd_window", "fa_fwd_varlen", "fa_bwd",
            "attention_backward", "fa_std_fwd", "fa_quantize_fp8", "fa_fp8_vt_cols", "fa_fwd_fp8",
            "quantize_fp8", "attention_fp8",
-           "fa_std_workspace_bytes", "fa_status_string", "fa_last_error", "attention",
+           "fa_std_workspace_bytes", "fa_status_string", "fa_last_error", "fa_build_info", "attention",
            "varlen_attention", "standard_attention", "library_path", "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -105,6 +105,8 @@ def load_library():
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_build_info.argtypes = []
+    lib.fa_build_info.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -132,6 +134,10 @@ def fa_status_string(status: int) -> str:
 
 def fa_last_error() -> str:
     return load_library().fa_last_error().decode()
+
+
+def fa_build_info() -> str:
+    return load_library().fa_build_info().decode()
 
 
 def _call(name, q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_seqlens, stream):

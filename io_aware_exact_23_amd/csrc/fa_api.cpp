@@ -437,6 +437,13 @@ extern "C" const char* fa_status_string(int status) {
 
 extern "C" const char* fa_last_error(void) { return g_last_error; }
 
+#define FA_STR2(x) #x
+#define FA_STR(x) FA_STR2(x)
+extern "C" const char* fa_build_info(void) {
+  return "compiler: clang " __clang_version__ "; HIP headers " FA_STR(HIP_VERSION_MAJOR) "." FA_STR(
+      HIP_VERSION_MINOR) "." FA_STR(HIP_VERSION_PATCH) "; device code: gfx950, packed fp32 VALU ops disabled";
+}
+
 extern "C" int fa_fp8_vt_cols(int Nk) { return Nk <= 0 ? 0 : (int)(((int64_t)Nk + 63) / 64 * 64); }
 
 extern "C" int fa_quantize_fp8(const void* x, void* y, float* descale, int B, int H, int N, int d,

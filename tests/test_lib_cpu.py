@@ -23,7 +23,7 @@ def declared_functions():
 
 
 def test_header_declares_the_abi():
-    assert declared_functions() == ["fa_bwd", "fa_fp8_vt_cols", "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8",
+    assert declared_functions() == ["fa_build_info", "fa_bwd", "fa_fp8_vt_cols", "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8",
                                     "fa_fwd_noalloc", "fa_fwd_varlen", "fa_fwd_window", "fa_last_error",
                                     "fa_quantize_fp8", "fa_status_string", "fa_std_fwd",
                                     "fa_std_workspace_bytes"]
@@ -34,6 +34,12 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(fa.library_path())
     for name in declared_functions():
         assert hasattr(lib, name), name
+
+
+@needs_lib
+def test_build_info_names_compiler_and_target():
+    info = fa.fa_build_info()
+    assert "clang" in info and "gfx950" in info and "HIP headers" in info
 
 
 @needs_lib
