@@ -184,3 +184,29 @@ def test_backward_long_causal_16k_workload_two_heads():
     checked for finiteness only (the fp64 oracle takes about 12 s and 13 GB per head)."""
     w = configs.LONG_CAUSAL_16K
     _check_heads(w, [(0, 0), (w.B - 1, w.H - 1)])
+
+
+def _draw_bwd(i):
+    """Seeded random backward case i: (B, H, Nq, Nk, d, causal, lens, scale, std)."""
+    r = np.random.default_rng(31000 + i)
+    d = int(r.choice([64, 128]))
+    B, H = int(r.integers(1, 4)), int(r.integers(1, 4))
+    Nq = 1 if r.random() < 0.15 else int(r.integers(2, 600))
+    Nk = Nq if (Nq > 1 and r.random() < 0.5) else int(r.integers(1, 600))
+    causal = Nq == Nk and r.random() < 0.6
+    lens = [int(x) for x in r.integers(0, Nk + 6, size=B)] if r.random() < 0.5 else None
+    scale = float(d ** -0.5 * r.choice([1.0, 0.5, 1.5, -1.0]))
+    std = float(r.choice([0.5, 1.0]))
+    return B, H, Nq, Nk, d, causal, lens, scale, std
+
+
+RANDOM_BWD = [_draw_bwd(i) for i in range(16)]
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_BWD)))
+def test_backward_random_shapes(case):
+    """Seeded random shapes (Nq from 1, Nq != Nk, clamped and zero lengths, negative scales)
+    against the oracle's gradients at the bars above."""
+    B, H, Nq, Nk, d, causal, lens, scale, std = RANDOM_BWD[case]
+    run_case(B, H, Nq, Nk, d, causal, lens, seed=50000 + 13 * case, std=std, scale=scale,
+             what=f"random {case}: {B}x{H}x{Nq}x{Nk} d={d} causal={causal} lens={lens} scale={scale:.4f} std={std}")
