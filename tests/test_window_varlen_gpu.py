@@ -214,3 +214,33 @@ def test_packed_16k_workload_sampled_rows():
     lg = torch.stack([lse[:, b * w.Nq + rt] for b in range(w.B)])
     compare(to_f64(og), to_f64(lg), o_ref, lse_ref, "bf16", what=f"{w.name} packed sampled rows")
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def _draw_varlen(i):
+    """Seeded random packed batch i: per-sequence query and key lengths (queries <= keys, some
+    empty, some past 2048), H, d and a window."""
+    r = np.random.default_rng(47000 + i)
+    n = int(r.integers(1, 7))
+    lens_k = [int(x) for x in r.integers(0, 2600 if r.random() < 0.3 else 700, size=n)]
+    same = r.random() < 0.6
+    lens_q = list(lens_k) if same else [int(r.integers(0, lk + 1)) for lk in lens_k]
+    H, d = int(r.integers(1, 4)), int(r.choice([64, 128]))
+    kind = r.integers(0, 4)
+    window = [(-1, -1), (-1, 0), (int(r.integers(0, 600)), 0),
+              (int(r.integers(0, 300)), int(r.integers(0, 300)))][kind]
+    return lens_q, lens_k, H, d, window
+
+
+RANDOM_VARLEN = [_draw_varlen(i) for i in range(12)]
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_VARLEN)))
+def test_varlen_random_batches(case):
+    """Seeded random packed batches against the oracle, sequence by sequence."""
+    lens_q, lens_k, H, d, window = RANDOM_VARLEN[case]
+    q, k, v, cq, ck = _packed(lens_q, lens_k, H, d, seed=700 + 11 * case)
+    what = f"random varlen {case}: q {lens_q} k {lens_k} H={H} d={d} window={window}"
+    print(what, flush=True)
+    o, lse = fa.varlen_attention(q, k, v, cq, ck, max(max(lens_q), 1), window=window)
+    torch.cuda.synchronize()
+    _check_packed(q, k, v, cq, ck, d ** -0.5, window, o, lse, what)
