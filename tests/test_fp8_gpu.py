@@ -301,3 +301,32 @@ def test_fp8_long_causal_workload_sampled_rows():
     rows = np.array([0, 1, 63, 64, 255, 256, 4095, 8191, 8192, 12345, 16127, 16128, 16383])
     check_fp8(o[:, :, rows], lse[:, :, rows], q8, k8, vt8, sq, sk, sv, w.scale, True, None,
               rows=rows, what="fp8 " + w.name)
+
+
+def _draw_fp8(i):
+    """Seeded random e4m3 case i: (B, H, Nq, Nk, d, causal, lens, scale, std)."""
+    r = np.random.default_rng(63000 + i)
+    d = int(r.choice([64, 128]))
+    B, H = int(r.integers(1, 4)), int(r.integers(1, 4))
+    Nq = 1 if r.random() < 0.15 else int(r.integers(2, 900))
+    Nk = Nq if (Nq > 1 and r.random() < 0.5) else int(r.integers(1, 900))
+    causal = Nq == Nk and r.random() < 0.6
+    lens = [int(x) for x in r.integers(0, Nk + 1, size=B)] if r.random() < 0.5 else None
+    scale = float(d ** -0.5 * r.choice([1.0, 0.5, 1.5, -1.0]))
+    std = float(r.choice([0.5, 1.0, 2.0]))
+    return B, H, Nq, Nk, d, causal, lens, scale, std
+
+
+RANDOM_FP8 = [_draw_fp8(i) for i in range(12)]
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_FP8)))
+def test_fp8_random_shapes(case):
+    """Seeded random shapes (one query row, Nq != Nk, zero lengths, negative scales, wider
+    spreads) against the oracle under the derived tolerance."""
+    B, H, Nq, Nk, d, causal, lens, scale, std = RANDOM_FP8[case]
+    what = f"fp8 random {case}: {B}x{H}x{Nq}x{Nk} d={d} causal={causal} lens={lens} scale={scale:.4f} std={std}"
+    print(what, flush=True)
+    q8, k8, vt8, sq, sk, sv = _make_fp8(B, H, Nq, Nk, d, seed=81000 + 7 * case, std=std, lens=lens)
+    o, lse = _run_fp8(q8, k8, vt8, sq, sk, sv, scale, causal, lens)
+    check_fp8(o, lse, q8, k8, vt8, sq, sk, sv, scale, causal, lens, what=what)
