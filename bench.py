@@ -8,9 +8,10 @@ the same run and reported under "decode". Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode]
                   [--no-short] [--no-standard] [--no-masks] [--no-backward] [--no-fp8]
-                  [--no-cpu-baseline] [--cpu-seconds S] [--calibrate-copy]
+                  [--no-gemm-reference] [--no-cpu-baseline] [--cpu-seconds S] [--calibrate-copy]
 
-"run" records the GPU, its peak engine clock, the ROCm, HIP and hipcc versions and the host CPU.
+"run" records the GPU, its peak engine clock, the ROCm and HIP versions, the compiler and target the
+library was built with (fa_build_info) and the host CPU.
 "cpu_baseline" is the fp64 oracle timed on a bounded sample of the workload on the host cores;
 "parity" compares the GPU output of the last timed step with the oracle on the same rows.
 "short_prefill" times the GPT-2- and BERT-shaped workloads per launch from a replayed HIP graph
@@ -25,7 +26,9 @@ are timed on the long workload's shape and reported under "masks": a causal slid
 fa_bwd, is timed on the 16K causal and GPT-2 shapes and reported under "backward", its FLOPs
 counted as the five products of the gradient. The e4m3 path (fa_quantize_fp8 + fa_fwd_fp8) is
 timed on the 16K causal shape and reported under "fp8" with its roofline against the fp8 matrix
-peak, the conversion cost, and its output's distance from the bf16 path's.
+peak, the conversion cost, and its output's distance from the bf16 path's. "gemm_reference" is a
+plain dense bf16 GEMM through torch.matmul on random operands, reported for context beside the
+matrix-core fractions (what a vendor-tuned library sustains on the same box).
 
 FLOPs are counted as 4*B*H*Nq*Nk*d, halved for causal masking. Decode bytes are the algorithmic
 HBM bytes: Q, the valid K and V rows, O and lse.
@@ -525,6 +528,29 @@ def bench_short_prefill(fa, configs, inputs, torch, dev, warmup):
     return out
 
 
+def bench_gemm_reference(torch, dev, warmup):
+    """Context for the matrix-core fractions: plain dense bf16 GEMMs (torch.matmul, the vendor
+    library) on random N(0,1) square operands, timed like the kernels. It is what a tuned library
+    sustains on the same box and data, not part of the attention path."""
+    out = {"what": "torch.matmul bf16 on random N(0,1) square operands [n, n] x [n, n]", "shapes": []}
+    for n in (8192, 16384):
+        a = torch.randn((n, n), device=dev, dtype=torch.float32).to(torch.bfloat16).contiguous()
+        b = torch.randn((n, n), device=dev, dtype=torch.float32).to(torch.bfloat16).contiguous()
+        c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+
+        def run():
+            torch.matmul(a, b, out=c)
+
+        _, per = time_launches(run, 10, max(warmup, 3), torch)
+        avg = float(np.mean(per))
+        fl = 2 * n ** 3
+        out["shapes"].append({"n": n, "ms_per_call": round(avg * 1e3, 4), "TFLOP/s": round(fl / avg / 1e12, 1),
+                              "frac_of_peak": round(fl / avg / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4)})
+        del a, b, c
+        torch.cuda.empty_cache()
+    return out
+
+
 def decode_bytes(w, lens) -> int:
     per_key = 2 * w.d * 2                      # one K row and one V row, bf16
     per_bh = 2 * w.d * 2 + 4                   # Q and O rows (bf16) and lse (fp32)
@@ -544,6 +570,8 @@ def main():
                     help="skip the sliding-window and packed-sequence timings")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass timing (fa_bwd)")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the dense bf16 GEMM reference (torch.matmul) reported for context")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the e4m3 forward timing (fa_quantize_fp8, fa_fwd_fp8)")
     ap.add_argument("--no-short", action="store_true",
@@ -673,6 +701,9 @@ def main():
     if not args.no_standard and w.Nq > 1 and w.dtype == "bf16":
         result["standard_attention"] = bench_standard(fa, configs, inputs, torch, dev, args.steps,
                                                       args.warmup, w.name)
+
+    if not args.no_gemm_reference:
+        result["gemm_reference"] = bench_gemm_reference(torch, dev, args.warmup)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)  # 1 GiB
